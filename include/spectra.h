@@ -1,0 +1,199 @@
+/*
+ * spectra.h -- C ABI of the SPECTRA sparse-precision dequant-GEMV library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  The SPECTRA page ("SPECTRA: Sparse-Precision
+ * Exact Channel Tensor Reconstruction Architecture", abstract) describes a
+ * weight codec: per input channel, a fourth-moment (kurtosis) test on the
+ * weight column scaled by the upstream normalization gain sends heavy-tailed
+ * channels to exact floating-point storage, and the Gaussian bulk to Group-32
+ * 4-bit codes with per-group scales and bit-packed zero points; fused GPU
+ * kernels then dequantize inside the matrix-vector product at decode batch
+ * sizes (same page, highlight 4, "High-Efficiency Fused ... Kernels").
+ * The page fixes neither formulas nor a memory layout.  Every choice below that
+ * it leaves open is stated where it is made, as this library's reading.
+ *
+ * Shapes: W is [N][K] (an nn.Linear weight: N outputs, K inputs, K contiguous),
+ * gamma is [K], x is [M][K], y is [M][N], all fp16 (IEEE binary16 bit patterns).
+ * y = x W^T with W replaced by its SPECTRA reconstruction.
+ *
+ * ---------------------------------------------------------------------------
+ * Quantization (what spectra_pack computes; all arithmetic in IEEE binary64
+ * unless stated; rint = round half to even; fp16() = round to nearest even)
+ * ---------------------------------------------------------------------------
+ *  1. Saliency and split.  For each input channel k: s[n] = W[n][k]*gamma[k]
+ *     (exact in binary64).  mean = sum_n s[n] / N; m2 = sum_n (s[n]-mean)^2 / N;
+ *     m4 = sum_n ((s[n]-mean)^2)^2 / N.  Channel k is heavy-tailed iff m2 > 0
+ *     and m4/(m2*m2) - 3 > 3.0 (excess kurtosis with population moments; the
+ *     page gives only "kurtosis > 3.0" -- this library reads it as excess
+ *     kurtosis, under which Gaussian columns are essentially never flagged).
+ *     A constant column (N = 1, gamma[k] = 0, ...) has m2 = 0 and is bulk.
+ *     The device evaluates the sums in a fixed tree order, so a channel whose
+ *     kurtosis lies within a few ulp of the threshold may be classified
+ *     differently from a sequential evaluation.
+ *  2. Order.  perm[0..K_b) lists the bulk channels ascending, perm[K_b..K) the
+ *     heavy-tailed channels ascending; n_out = K - K_b; G = ceil(K_b / 32).
+ *     Bulk position j of row n holds W[n][perm[j]]; group g = positions
+ *     [32g, 32g+32); positions >= K_b are padding.
+ *  3. Per group (n, g), over its real members w (padding excluded):
+ *       lo = min(0, min w), hi = max(0, max w), s = (hi - lo) / 15,
+ *       s16 = fp16(s).
+ *     If s16 == 0: z = 0 and every code is 0.  Otherwise
+ *       z = min(15, rint(-lo / s16)),  q = min(15, max(0, rint(w / s16) + z)).
+ *     Padding members get q = z.
+ *  4. Reconstruction: w_hat = (q - z) * s16 (exact in binary32 and binary64).
+ *     Heavy-tailed channels are not quantized: O[n][j] = W[n][perm[K_b+j]]
+ *     bit for bit (no gain applied, no rounding).
+ *  5. Product (spectra_gemm): y[m][n] = sum_{j<K_b} x[m][perm[j]] * w_hat[n][j]
+ *     + sum_{j<n_out} x[m][perm[K_b+j]] * O[n][j], accumulated in binary32 and
+ *     rounded to fp16.  The accuracy contract is, per element,
+ *     |y - y_exact| <= 1e-3 * sum_k |W_hat[n][k]| * |x[m][k]| + 1e-6.
+ *
+ * ---------------------------------------------------------------------------
+ * Container image (little-endian).  This is both the device-resident layout
+ * and the byte stream spectra_export returns.
+ * ---------------------------------------------------------------------------
+ *  Header, 128 bytes:
+ *    [0,4)    magic   u32 = 0x31435053 (bytes 'S' 'P' 'C' '1')
+ *    [4,8)    version u32 = 1
+ *    [8,16)   K       i64     [16,24)  N     i64     [24,32)  K_b   i64
+ *    [32,40)  G       i64     [40,48)  n_out i64
+ *    [48,56)  off_mask     u64    [56,64)  off_perm     u64
+ *    [64,72)  off_codes    u64    [72,80)  off_scales   u64
+ *    [80,88)  off_zeros    u64    [88,96)  off_outliers u64
+ *    [96,104) total_bytes  u64    [104,128) zero
+ *  Sections follow in the order below.  Each starts at the smallest multiple
+ *  of 256 that is not below the end of the previous one (the header ends at
+ *  128); total_bytes is the end of the last section rounded up to a multiple
+ *  of 256.  Every padding byte is zero.  An empty section has size 0.
+ *    mask     ceil(K/32) x u32.  Bit (k mod 32) of word floor(k/32) is 1 iff
+ *             channel k is heavy-tailed.
+ *    perm     K x i32, as in step 2.
+ *    codes    N*G records of 16 bytes; the record of group (n, g) starts at
+ *             byte 16*(n*G + g) and is four u32 words.  Member e (0..31) of the
+ *             group is the 4-bit field of word floor(e/8) starting at bit
+ *             16*(e mod 2) + 4*floor((e mod 8)/2).  (So (word >> 4i) & 0x000F000F
+ *             holds members 8d+2i and 8d+2i+1 in its two 16-bit halves.)
+ *    scales   N*G x fp16: s16 of group (n, g) at index n*G + g.
+ *    zeros    ceil(N*G/2) bytes: z of flat group index i = n*G + g is in byte
+ *             floor(i/2), bits [4*(i mod 2), 4*(i mod 2) + 4).
+ *    outliers N x n_out fp16, row-major: O[n][j] at index n*n_out + j.
+ *  Payload bytes (codes + scales + zeros + outliers, unpadded) are
+ *  16*N*G + 2*N*G + ceil(N*G/2) + 2*N*n_out: 4 + 16/32 + 4/32 bits per bulk
+ *  weight (K_b rounded up to 32G) plus 16 bits per heavy-tailed weight.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions
+ * ---------------------------------------------------------------------------
+ *  - Functions returning int return SPECTRA_OK or a negative spectra_status.
+ *    No exception or abort crosses the ABI.  spectra_last_error() returns a
+ *    thread-local message describing the latest failure on the calling thread.
+ *  - A container owns one device allocation on the device that was current
+ *    when it was packed; it is immutable after packing and may be used by
+ *    concurrent spectra_gemm* calls on any streams of that device.
+ *  - x and y are caller-owned device buffers; the library never retains them.
+ *  - gemm calls are asynchronous: launch errors are returned, device faults
+ *    surface at the caller's next synchronization.
+ */
+#ifndef SPECTRA_H
+#define SPECTRA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spectra_container spectra_container;
+
+typedef enum {
+  SPECTRA_OK = 0,
+  SPECTRA_E_INVAL = -1,        /* bad argument: null pointer, size out of range, misalignment, freed container */
+  SPECTRA_E_NONFINITE = -2,    /* W or gamma holds an infinity or a NaN */
+  SPECTRA_E_NOMEM = -3,        /* a device or host allocation failed */
+  SPECTRA_E_HIP = -4,          /* a HIP runtime call failed (message has the HIP error string) */
+  SPECTRA_E_UNSUPPORTED = -5   /* the forced kernel cannot run this shape */
+} spectra_status;
+
+/* Kernel selection for spectra_gemm_ex. */
+typedef enum {
+  SPECTRA_KERNEL_AUTO = 0,     /* GEMV for small M where it fits, MFMA otherwise */
+  SPECTRA_KERNEL_GEMV = 1,     /* VALU dequant-GEMV (register/LDS x, fp32 accumulate) */
+  SPECTRA_KERNEL_MFMA = 2      /* LDS-dequant tiles feeding v_mfma_f32_16x16x32_f16 */
+} spectra_kernel;
+
+typedef struct {
+  int64_t K, N, K_b, G, n_out;
+  uint64_t bytes_codes;        /* 16*N*G */
+  uint64_t bytes_scales;       /* 2*N*G */
+  uint64_t bytes_zeros;        /* ceil(N*G/2) */
+  uint64_t bytes_outliers;     /* 2*N*n_out */
+  uint64_t bytes_payload;      /* sum of the four above */
+  uint64_t bytes_meta;         /* 128 + 4*ceil(K/32) + 4*K (header, mask, perm; unpadded) */
+  uint64_t bytes_total;        /* whole image including alignment padding (= total_bytes) */
+} spectra_info_t;
+
+/* Limits on the shapes spectra_pack accepts. */
+#define SPECTRA_MAX_K ((int64_t)1 << 24)
+#define SPECTRA_MAX_N ((int64_t)1 << 31)
+#define SPECTRA_MAX_M ((int64_t)1 << 20)
+
+/* Pack W (HOST memory, [N][K] fp16 bits, row-major) with gain gamma (HOST
+ * memory, [K] fp16 bits) into a new device-resident container on the current
+ * device.  The inputs are borrowed for the duration of the call only.
+ * Synchronous: the container is complete when the call returns.
+ * Requires 1 <= K <= SPECTRA_MAX_K and 1 <= N <= SPECTRA_MAX_N.
+ * Returns NULL on error (E_INVAL, E_NONFINITE, E_NOMEM, E_HIP; see
+ * spectra_last_error).  The split, quantization and layout are the steps and
+ * the image described at the top of this file. */
+spectra_container* spectra_pack(const uint16_t* W, const uint16_t* gamma, int64_t K, int64_t N);
+
+/* As spectra_pack, but W and gamma are DEVICE pointers (current device) and the
+ * packing kernels run on `stream` (a hipStream_t; NULL = null stream).  The
+ * call still returns only once the container is complete. */
+spectra_container* spectra_pack_device(const void* W, const void* gamma, int64_t K, int64_t N,
+                                       void* stream);
+
+/* y = x W_hat^T.  x: DEVICE fp16 [M][K] contiguous, y: DEVICE fp16 [M][N]
+ * contiguous, overwritten; both 4-byte aligned, on the container's device.
+ * 1 <= M <= SPECTRA_MAX_M.  Enqueued on the null stream; returns at once. */
+int spectra_gemm(const spectra_container* c, const void* x, void* y, int64_t M);
+
+/* As spectra_gemm, enqueued on `stream` (a hipStream_t; NULL = null stream),
+ * with the kernel chosen by `kernel` (a spectra_kernel).  A forced kernel that
+ * cannot run the shape returns SPECTRA_E_UNSUPPORTED and enqueues nothing. */
+int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t M,
+                    void* stream, int kernel);
+
+/* Several containers that share K and the same input x (e.g. the q/k/v or the
+ * gate/up projections of one decoder layer) in one launch: ys[i] = x W_i^T.
+ * cs and ys are HOST arrays of `count` entries (1 <= count <= 64); every ys[i]
+ * is a DEVICE fp16 [M][N_i] buffer.  Runs on `stream`; returns at once.  Same
+ * result, element for element, as `count` spectra_gemm_ex calls with the
+ * GEMV kernel; M must be 1. */
+int spectra_gemm_grouped(const spectra_container* const* cs, int count, const void* x,
+                         void* const* ys, int64_t M, void* stream);
+
+/* Release the container and its device memory.  NULL-safe.  The handle is
+ * poisoned first, so a later call with it returns SPECTRA_E_INVAL rather than
+ * touching freed memory (as long as the host memory was not reused). */
+void spectra_free(spectra_container* c);
+
+/* Shape and byte counts of a container. */
+int spectra_info(const spectra_container* c, spectra_info_t* out);
+
+/* Copy the container image (header + sections, total_bytes) to HOST memory
+ * host_dst of capacity cap bytes.  E_INVAL if cap < total_bytes.  Synchronous. */
+int spectra_export(const spectra_container* c, void* host_dst, uint64_t cap);
+
+/* Thread-local description of the latest error on the calling thread ("" if none). */
+const char* spectra_last_error(void);
+
+/* ABI version (1). */
+int spectra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECTRA_H */
