@@ -1,0 +1,347 @@
+// Host side of libspectra: the extern "C" entry points declared in
+// include/spectra.h -- argument checks, the container's device allocation and
+// header, packing orchestration and kernel dispatch.  Every computation on
+// the data runs in the device kernels of pack.hip, gemv.hip and mfma.hip.
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <new>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/spectra.h"
+#include "spectra_internal.h"
+
+namespace spectra {
+
+namespace {
+thread_local std::string g_last_error;
+
+struct PropsCache {
+  std::mutex mu;
+  std::vector<DeviceProps> props;
+  std::vector<bool> have;
+};
+PropsCache& props_cache() {
+  static PropsCache pc;
+  return pc;
+}
+}  // namespace
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int fail(int status, const std::string& msg) {
+  set_error(msg);
+  return status;
+}
+
+const DeviceProps& device_props(int device) {
+  PropsCache& pc = props_cache();
+  std::lock_guard<std::mutex> lk(pc.mu);
+  if ((int)pc.props.size() <= device) {
+    pc.props.resize(device + 1);
+    pc.have.resize(device + 1, false);
+  }
+  if (!pc.have[device]) {
+    hipDeviceProp_t p;
+    DeviceProps d{256, 64 * 1024};
+    if (hipGetDeviceProperties(&p, device) == hipSuccess) {
+      d.cu_count = p.multiProcessorCount > 0 ? p.multiProcessorCount : 256;
+      d.lds_per_block = p.sharedMemPerBlock;
+    }
+    pc.props[device] = d;
+    pc.have[device] = true;
+  }
+  return pc.props[device];
+}
+
+namespace {
+
+std::string hip_msg(const char* what, hipError_t e) {
+  return std::string(what) + ": " + hipGetErrorString(e);
+}
+
+// Registry of live handles: a handle is checked by membership, so a freed or
+// foreign pointer is rejected without ever being dereferenced.
+struct Registry {
+  std::mutex mu;
+  std::unordered_set<const spectra_container*> live;
+};
+Registry& registry() {
+  static Registry r;
+  return r;
+}
+bool live(const spectra_container* c) {
+  if (c == nullptr) return false;
+  Registry& r = registry();
+  std::lock_guard<std::mutex> lk(r.mu);
+  return r.live.count(c) != 0;
+}
+void register_handle(const spectra_container* c) {
+  Registry& r = registry();
+  std::lock_guard<std::mutex> lk(r.mu);
+  r.live.insert(c);
+}
+bool unregister_handle(const spectra_container* c) {
+  Registry& r = registry();
+  std::lock_guard<std::mutex> lk(r.mu);
+  return r.live.erase(c) != 0;
+}
+
+// Frees device buffers on scope exit unless released.
+struct DevBuf {
+  void* p = nullptr;
+  ~DevBuf() {
+    if (p) (void)hipFree(p);
+  }
+  void* release() {
+    void* q = p;
+    p = nullptr;
+    return q;
+  }
+};
+
+int check_shape(int64_t K, int64_t N) {
+  if (K < 1 || K > SPECTRA_MAX_K) return fail(SPECTRA_E_INVAL, "K out of range [1, 2^24]");
+  if (N < 1 || N > SPECTRA_MAX_N) return fail(SPECTRA_E_INVAL, "N out of range [1, 2^31]");
+  // Keep every flat index and byte offset comfortably inside 63 bits and the
+  // 1-D grids of the packing kernels inside their limits.
+  if ((double)K * (double)N > (double)(1ull << 40))
+    return fail(SPECTRA_E_INVAL, "N*K above 2^40 elements");
+  return SPECTRA_OK;
+}
+
+spectra_container* pack_impl(const uint16_t* W_dev, const uint16_t* g_dev, int64_t K, int64_t N,
+                             hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error(hip_msg("hipGetDevice", e));
+    return nullptr;
+  }
+  const uint64_t mask_words = (uint64_t)((K + 31) / 32);
+  DevBuf scratch, status;
+  e = hipMalloc(&scratch.p, kurtosis_scratch_bytes(K, N));
+  if (e != hipSuccess) {
+    set_error(hip_msg("hipMalloc (kurtosis scratch)", e));
+    return nullptr;
+  }
+  e = hipMalloc(&status.p, 4 * (1 + mask_words));
+  if (e != hipSuccess) {
+    set_error(hip_msg("hipMalloc (status)", e));
+    return nullptr;
+  }
+  uint32_t* st = static_cast<uint32_t*>(status.p);
+  if ((e = hipMemsetAsync(st, 0, 4 * (1 + mask_words), s)) != hipSuccess ||
+      (e = launch_kurtosis(W_dev, g_dev, K, N, scratch.p, st, s)) != hipSuccess) {
+    set_error(hip_msg("kurtosis launch", e));
+    return nullptr;
+  }
+  std::vector<uint32_t> host_status(1 + mask_words);
+  if ((e = hipMemcpyAsync(host_status.data(), st, 4 * (1 + mask_words), hipMemcpyDeviceToHost,
+                          s)) != hipSuccess ||
+      (e = hipStreamSynchronize(s)) != hipSuccess) {
+    set_error(hip_msg("kurtosis readback", e));
+    return nullptr;
+  }
+  if (host_status[0] & 1u) {
+    set_error("W or gamma holds a non-finite value");
+    return nullptr;
+  }
+  int64_t n_out = 0;
+  for (uint64_t w = 0; w < mask_words; ++w) n_out += __builtin_popcount(host_status[1 + w]);
+
+  spectra_container* c = new (std::nothrow) spectra_container();
+  if (!c) {
+    set_error("host allocation of the container handle failed");
+    return nullptr;
+  }
+  c->tag = kLiveTag;
+  c->device = dev;
+  c->K = K;
+  c->N = N;
+  c->n_out = n_out;
+  c->K_b = K - n_out;
+  c->G = (c->K_b + kGroup - 1) / kGroup;
+  c->lay = make_layout(K, N, n_out);
+  DevBuf img;
+  e = hipMalloc(&img.p, c->lay.total);
+  if (e != hipSuccess) {
+    delete c;
+    set_error(hip_msg("hipMalloc (container)", e));
+    return nullptr;
+  }
+  c->dev = static_cast<unsigned char*>(img.p);
+
+  uint64_t hdr[kHeaderBytes / 8];
+  memset(hdr, 0, sizeof(hdr));
+  hdr[0] = (uint64_t)kMagic | ((uint64_t)kVersion << 32);
+  hdr[1] = (uint64_t)K;
+  hdr[2] = (uint64_t)N;
+  hdr[3] = (uint64_t)c->K_b;
+  hdr[4] = (uint64_t)c->G;
+  hdr[5] = (uint64_t)n_out;
+  hdr[6] = c->lay.mask;
+  hdr[7] = c->lay.perm;
+  hdr[8] = c->lay.codes;
+  hdr[9] = c->lay.scales;
+  hdr[10] = c->lay.zeros;
+  hdr[11] = c->lay.outliers;
+  hdr[12] = c->lay.total;
+  if ((e = hipMemsetAsync(c->dev, 0, c->lay.total, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(c->dev, hdr, sizeof(hdr), hipMemcpyHostToDevice, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(c->dev + c->lay.mask, st + 1, 4 * mask_words, hipMemcpyDeviceToDevice,
+                          s)) != hipSuccess ||
+      (e = launch_quantize(W_dev, c, s)) != hipSuccess ||
+      (e = hipStreamSynchronize(s)) != hipSuccess) {
+    delete c;
+    set_error(hip_msg("packing", e));
+    return nullptr;
+  }
+  img.release();
+  register_handle(c);
+  return c;
+}
+
+}  // namespace
+}  // namespace spectra
+
+using namespace spectra;
+
+extern "C" {
+
+int spectra_version(void) { return 1; }
+
+const char* spectra_last_error(void) { return g_last_error.c_str(); }
+
+spectra_container* spectra_pack_device(const void* W, const void* gamma, int64_t K, int64_t N,
+                                       void* stream) {
+  set_error("");
+  if (!W || !gamma) {
+    set_error("null W or gamma");
+    return nullptr;
+  }
+  if (check_shape(K, N) != SPECTRA_OK) return nullptr;
+  return pack_impl(static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(gamma), K, N,
+                   static_cast<hipStream_t>(stream));
+}
+
+spectra_container* spectra_pack(const uint16_t* W, const uint16_t* gamma, int64_t K, int64_t N) {
+  set_error("");
+  if (!W || !gamma) {
+    set_error("null W or gamma");
+    return nullptr;
+  }
+  if (check_shape(K, N) != SPECTRA_OK) return nullptr;
+  DevBuf wd, gd;
+  hipError_t e;
+  const size_t wbytes = 2ull * (uint64_t)N * (uint64_t)K;
+  if ((e = hipMalloc(&wd.p, wbytes)) != hipSuccess || (e = hipMalloc(&gd.p, 2ull * K)) != hipSuccess) {
+    set_error(hip_msg("hipMalloc (staging W/gamma)", e));
+    return nullptr;
+  }
+  if ((e = hipMemcpy(wd.p, W, wbytes, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(gd.p, gamma, 2ull * K, hipMemcpyHostToDevice)) != hipSuccess) {
+    set_error(hip_msg("upload W/gamma", e));
+    return nullptr;
+  }
+  return pack_impl(static_cast<const uint16_t*>(wd.p), static_cast<const uint16_t*>(gd.p), K, N,
+                   nullptr);
+}
+
+void spectra_free(spectra_container* c) {
+  if (!unregister_handle(c)) return;
+  c->tag = kDeadTag;
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  if (cur != c->device) (void)hipSetDevice(c->device);
+  (void)hipFree(c->dev);
+  if (cur >= 0 && cur != c->device) (void)hipSetDevice(cur);
+  c->dev = nullptr;
+  delete c;
+}
+
+int spectra_info(const spectra_container* c, spectra_info_t* out) {
+  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+  if (!out) return fail(SPECTRA_E_INVAL, "null info pointer");
+  const uint64_t NG = (uint64_t)c->N * (uint64_t)c->G;
+  out->K = c->K;
+  out->N = c->N;
+  out->K_b = c->K_b;
+  out->G = c->G;
+  out->n_out = c->n_out;
+  out->bytes_codes = 16 * NG;
+  out->bytes_scales = 2 * NG;
+  out->bytes_zeros = (NG + 1) / 2;
+  out->bytes_outliers = 2ull * (uint64_t)c->N * (uint64_t)c->n_out;
+  out->bytes_payload = out->bytes_codes + out->bytes_scales + out->bytes_zeros + out->bytes_outliers;
+  out->bytes_meta = kHeaderBytes + 4ull * (uint64_t)((c->K + 31) / 32) + 4ull * (uint64_t)c->K;
+  out->bytes_total = c->lay.total;
+  return SPECTRA_OK;
+}
+
+int spectra_export(const spectra_container* c, void* host_dst, uint64_t cap) {
+  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+  if (!host_dst) return fail(SPECTRA_E_INVAL, "null destination");
+  if (cap < c->lay.total) return fail(SPECTRA_E_INVAL, "destination smaller than total_bytes");
+  hipError_t e = hipMemcpy(host_dst, c->dev, c->lay.total, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("export copy", e));
+  return SPECTRA_OK;
+}
+
+int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t M, void* stream,
+                    int kernel) {
+  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+  if (!x || !y) return fail(SPECTRA_E_INVAL, "null x or y");
+  if ((reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(y) & 3))
+    return fail(SPECTRA_E_INVAL, "x and y must be 4-byte aligned");
+  if (M < 1 || M > SPECTRA_MAX_M) return fail(SPECTRA_E_INVAL, "M out of range [1, 2^20]");
+  if (kernel < SPECTRA_KERNEL_AUTO || kernel > SPECTRA_KERNEL_MFMA)
+    return fail(SPECTRA_E_INVAL, "unknown kernel selector");
+  const DeviceView v = c->view();
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  uint16_t* yp = static_cast<uint16_t*>(y);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (kernel == SPECTRA_KERNEL_GEMV || (kernel == SPECTRA_KERNEL_AUTO && gemv_supports(v, M))) {
+    if (!gemv_supports(v, M)) return fail(SPECTRA_E_UNSUPPORTED, "GEMV kernel cannot run this shape");
+    e = launch_gemv(v, xp, yp, M, s);
+  } else {
+    if (!mfma_supports(v, M)) return fail(SPECTRA_E_UNSUPPORTED, "MFMA kernel cannot run this shape");
+    e = launch_mfma(v, xp, yp, M, s);
+  }
+  if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("kernel launch", e));
+  return SPECTRA_OK;
+}
+
+int spectra_gemm(const spectra_container* c, const void* x, void* y, int64_t M) {
+  return spectra_gemm_ex(c, x, y, M, nullptr, SPECTRA_KERNEL_AUTO);
+}
+
+int spectra_gemm_grouped(const spectra_container* const* cs, int count, const void* x,
+                         void* const* ys, int64_t M, void* stream) {
+  if (!cs || !ys || !x) return fail(SPECTRA_E_INVAL, "null argument");
+  if (count < 1 || count > 64) return fail(SPECTRA_E_INVAL, "count out of range [1, 64]");
+  if (M != 1) return fail(SPECTRA_E_UNSUPPORTED, "grouped launch supports M = 1");
+  DeviceView vs[64];
+  for (int i = 0; i < count; ++i) {
+    if (!live(cs[i])) return fail(SPECTRA_E_INVAL, "invalid or freed container in group");
+    if (!ys[i] || (reinterpret_cast<uintptr_t>(ys[i]) & 3))
+      return fail(SPECTRA_E_INVAL, "null or misaligned y in group");
+    if (cs[i]->K != cs[0]->K || cs[i]->device != cs[0]->device)
+      return fail(SPECTRA_E_INVAL, "grouped containers must share K and device");
+    vs[i] = cs[i]->view();
+    if (!gemv_supports(vs[i], 1))
+      return fail(SPECTRA_E_UNSUPPORTED, "GEMV kernel cannot run a container of the group");
+  }
+  if (reinterpret_cast<uintptr_t>(x) & 3) return fail(SPECTRA_E_INVAL, "x must be 4-byte aligned");
+  hipError_t e = launch_gemv_grouped(vs, count, static_cast<const uint16_t*>(x),
+                                     reinterpret_cast<uint16_t* const*>(ys),
+                                     static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(SPECTRA_E_UNSUPPORTED, "grouped launch not available");
+  if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("grouped launch", e));
+  return SPECTRA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Internal declarations shared by the host ABI and the gfx950 kernels of
+// libspectra.  Not part of the public interface (include/spectra.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace spectra {
+
+constexpr uint32_t kMagic = 0x31435053u;          // 'S' 'P' 'C' '1'
+constexpr uint32_t kVersion = 1;
+constexpr uint64_t kHeaderBytes = 128;
+constexpr uint64_t kAlign = 256;
+constexpr int kGroup = 32;
+constexpr uint64_t kLiveTag = 0x5350454354524131ull;  // host handle tag while alive
+constexpr uint64_t kDeadTag = 0xDEADDEADDEADDEADull;  // written by spectra_free
+
+// Offsets of the six sections inside the container image.
+struct Layout {
+  uint64_t mask, perm, codes, scales, zeros, outliers, total;
+};
+
+inline uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline Layout make_layout(int64_t K, int64_t N, int64_t n_out) {
+  const int64_t K_b = K - n_out;
+  const int64_t G = (K_b + kGroup - 1) / kGroup;
+  const uint64_t NG = (uint64_t)N * (uint64_t)G;
+  Layout L;
+  uint64_t pos = kHeaderBytes;
+  pos = align_up(pos); L.mask = pos; pos += 4ull * (uint64_t)((K + 31) / 32);
+  pos = align_up(pos); L.perm = pos; pos += 4ull * (uint64_t)K;
+  pos = align_up(pos); L.codes = pos; pos += 16ull * NG;
+  pos = align_up(pos); L.scales = pos; pos += 2ull * NG;
+  pos = align_up(pos); L.zeros = pos; pos += (NG + 1) / 2;
+  pos = align_up(pos); L.outliers = pos; pos += 2ull * (uint64_t)N * (uint64_t)n_out;
+  L.total = align_up(pos);
+  return L;
+}
+
+// Device-side view of one container, passed by value to kernels.
+struct DeviceView {
+  const uint4* codes;        // [N*G] 16-byte records
+  const uint16_t* scales;    // [N*G] fp16 bits
+  const uint8_t* zeros;      // [ceil(N*G/2)] nibbles
+  const uint16_t* outliers;  // [N][n_out] fp16 bits
+  const int32_t* perm;       // [K]
+  int64_t N;
+  int32_t K, K_b, G, n_out;
+  int32_t cu_count;          // compute units of the container's device (launch sizing)
+};
+
+// Per-device properties the launchers need.
+struct DeviceProps {
+  int cu_count;
+  size_t lds_per_block;
+};
+const DeviceProps& device_props(int device);
+
+}  // namespace spectra
+
+struct spectra_container {
+  uint64_t tag;
+  int device;
+  int64_t K, N, K_b, G, n_out;
+  spectra::Layout lay;
+  unsigned char* dev;  // one device allocation holding the whole image
+  spectra::DeviceView view() const {
+    spectra::DeviceView v;
+    v.codes = reinterpret_cast<const uint4*>(dev + lay.codes);
+    v.scales = reinterpret_cast<const uint16_t*>(dev + lay.scales);
+    v.zeros = reinterpret_cast<const uint8_t*>(dev + lay.zeros);
+    v.outliers = reinterpret_cast<const uint16_t*>(dev + lay.outliers);
+    v.perm = reinterpret_cast<const int32_t*>(dev + lay.perm);
+    v.N = N;
+    v.K = (int32_t)K;
+    v.K_b = (int32_t)K_b;
+    v.G = (int32_t)G;
+    v.n_out = (int32_t)n_out;
+    v.cu_count = spectra::device_props(device).cu_count;
+    return v;
+  }
+};
+
+namespace spectra {
+
+void set_error(const std::string& msg);
+int fail(int status, const std::string& msg);
+
+// ---- packer (pack.hip) ----
+// Scratch needed by the kurtosis passes for a K x N matrix, in bytes.
+uint64_t kurtosis_scratch_bytes(int64_t K, int64_t N);
+// Runs the split passes; writes ceil(K/32) mask words and one status word
+// (bit 0: non-finite input seen) into `status_out` (device, (1 + ceil(K/32)) u32).
+hipError_t launch_kurtosis(const uint16_t* W, const uint16_t* gamma, int64_t K, int64_t N,
+                           void* scratch, uint32_t* status_out, hipStream_t s);
+// Fills perm, codes, scales, zeros and outliers of a container whose header and
+// mask are already in place.
+hipError_t launch_quantize(const uint16_t* W, const spectra_container* c, hipStream_t s);
+
+// ---- product kernels (gemv.hip, mfma.hip) ----
+// Return hipErrorNotSupported (without launching) when the kernel cannot run the shape.
+bool gemv_supports(const DeviceView& v, int64_t M);
+hipError_t launch_gemv(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M, hipStream_t s);
+hipError_t launch_gemv_grouped(const DeviceView* vs, int count, const uint16_t* x,
+                               uint16_t* const* ys, hipStream_t s);
+bool mfma_supports(const DeviceView& v, int64_t M);
+hipError_t launch_mfma(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M, hipStream_t s);
+
+}  // namespace spectra

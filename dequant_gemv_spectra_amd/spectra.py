@@ -1,0 +1,216 @@
+"""Python binding of libspectra (ctypes).  Argument marshalling only: every
+step of packing and of the product runs in the library's gfx950 kernels.
+
+Names mirror the C ABI in include/spectra.h.  PyTorch supplies device memory
+and streams; tensors cross the boundary as raw pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspectra.so")
+
+SPECTRA_OK = 0
+SPECTRA_E_INVAL = -1
+SPECTRA_E_NONFINITE = -2
+SPECTRA_E_NOMEM = -3
+SPECTRA_E_HIP = -4
+SPECTRA_E_UNSUPPORTED = -5
+
+KERNELS = {"auto": 0, "gemv": 1, "mfma": 2}
+
+EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm_ex",
+            "spectra_gemm_grouped", "spectra_free", "spectra_info", "spectra_export",
+            "spectra_last_error", "spectra_version"]
+
+
+class SpectraError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"spectra status {status}: {msg}")
+        self.status = status
+
+
+class spectra_info_t(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int64), ("N", ctypes.c_int64), ("K_b", ctypes.c_int64),
+                ("G", ctypes.c_int64), ("n_out", ctypes.c_int64),
+                ("bytes_codes", ctypes.c_uint64), ("bytes_scales", ctypes.c_uint64),
+                ("bytes_zeros", ctypes.c_uint64), ("bytes_outliers", ctypes.c_uint64),
+                ("bytes_payload", ctypes.c_uint64), ("bytes_meta", ctypes.c_uint64),
+                ("bytes_total", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree libspectra.so; fail loudly when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m dequant_gemv_spectra_amd.build` (needs ROCm hipcc)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, u64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int
+    L.spectra_pack.argtypes = [vp, vp, i64, i64]
+    L.spectra_pack.restype = vp
+    L.spectra_pack_device.argtypes = [vp, vp, i64, i64, vp]
+    L.spectra_pack_device.restype = vp
+    L.spectra_gemm.argtypes = [vp, vp, vp, i64]
+    L.spectra_gemm.restype = c_int
+    L.spectra_gemm_ex.argtypes = [vp, vp, vp, i64, vp, c_int]
+    L.spectra_gemm_ex.restype = c_int
+    L.spectra_gemm_grouped.argtypes = [ctypes.POINTER(vp), c_int, vp, ctypes.POINTER(vp), i64, vp]
+    L.spectra_gemm_grouped.restype = c_int
+    L.spectra_free.argtypes = [vp]
+    L.spectra_free.restype = None
+    L.spectra_info.argtypes = [vp, ctypes.POINTER(spectra_info_t)]
+    L.spectra_info.restype = c_int
+    L.spectra_export.argtypes = [vp, vp, u64]
+    L.spectra_export.restype = c_int
+    L.spectra_last_error.argtypes = []
+    L.spectra_last_error.restype = ctypes.c_char_p
+    L.spectra_version.argtypes = []
+    L.spectra_version.restype = c_int
+    _lib = L
+    return L
+
+
+def spectra_last_error() -> str:
+    return lib().spectra_last_error().decode()
+
+
+def _check(status: int):
+    if status != SPECTRA_OK:
+        raise SpectraError(status, spectra_last_error())
+
+
+class Container:
+    """Owning handle of a packed container (freed on close / garbage collection)."""
+
+    def __init__(self, ptr: int):
+        self.ptr = ptr
+        self._info = None
+
+    @property
+    def handle(self):
+        if not self.ptr:
+            raise SpectraError(SPECTRA_E_INVAL, "container already freed")
+        return ctypes.c_void_p(self.ptr)
+
+    def info(self) -> dict:
+        if self._info is None:
+            self._info = spectra_info(self)
+        return self._info
+
+    def close(self):
+        if self.ptr:
+            lib().spectra_free(ctypes.c_void_p(self.ptr))
+            self.ptr = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def spectra_pack(W, gamma, stream=None) -> Container:
+    """Pack fp16 W [N][K] with gain fp16 gamma [K].
+
+    numpy arrays and CPU tensors go through the host entry point; CUDA tensors
+    through the device entry point (on `stream`, default the current stream).
+    """
+    if isinstance(W, np.ndarray) or (hasattr(W, "is_cuda") and not W.is_cuda):
+        Wn = np.ascontiguousarray(np.asarray(W), dtype=np.float16)
+        gn = np.ascontiguousarray(np.asarray(gamma), dtype=np.float16)
+        if Wn.ndim != 2 or gn.shape != (Wn.shape[1],):
+            raise ValueError("W must be [N][K] and gamma [K]")
+        N, K = Wn.shape
+        p = lib().spectra_pack(Wn.ctypes.data_as(ctypes.c_void_p), gn.ctypes.data_as(ctypes.c_void_p),
+                               K, N)
+    else:
+        import torch
+        if W.dtype != torch.float16 or gamma.dtype != torch.float16:
+            raise ValueError("W and gamma must be float16")
+        W = W.contiguous()
+        gamma = gamma.contiguous()
+        N, K = W.shape
+        if gamma.shape != (K,) or not gamma.is_cuda:
+            raise ValueError("gamma must be a CUDA tensor of shape [K]")
+        p = lib().spectra_pack_device(ctypes.c_void_p(W.data_ptr()), ctypes.c_void_p(gamma.data_ptr()),
+                                      K, N, _stream_ptr(stream))
+    if not p:
+        msg = spectra_last_error()
+        status = SPECTRA_E_NONFINITE if "non-finite" in msg else SPECTRA_E_INVAL
+        raise SpectraError(status, msg)
+    return Container(p)
+
+
+def spectra_gemm(c: Container, x, y=None, stream=None, kernel: str = "auto"):
+    """y = x W_hat^T for CUDA fp16 x [M][K]; returns y (fp16 [M][N], allocated if None)."""
+    import torch
+    info = c.info()
+    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.shape[1] != info["K"]:
+        raise ValueError("x must be a CUDA float16 tensor of shape [M][K]")
+    x = x.contiguous()
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, info["N"]), dtype=torch.float16, device=x.device)
+    elif y.dtype != torch.float16 or not y.is_contiguous() or tuple(y.shape) != (M, info["N"]):
+        raise ValueError("y must be a contiguous float16 tensor of shape [M][N]")
+    _check(lib().spectra_gemm_ex(c.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                 M, _stream_ptr(stream), KERNELS[kernel]))
+    return y
+
+
+def spectra_gemm_grouped(cs, x, ys=None, stream=None):
+    """ys[i] = x W_i^T for containers sharing K, one launch; x is CUDA fp16 [1][K]."""
+    import torch
+    n = len(cs)
+    if ys is None:
+        ys = [torch.empty((x.shape[0], c.info()["N"]), dtype=torch.float16, device=x.device) for c in cs]
+    arr_c = (ctypes.c_void_p * n)(*[c.handle.value for c in cs])
+    arr_y = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    x = x.contiguous()
+    _check(lib().spectra_gemm_grouped(arr_c, n, ctypes.c_void_p(x.data_ptr()), arr_y, x.shape[0],
+                                      _stream_ptr(stream)))
+    return ys
+
+
+def spectra_free(c: Container):
+    c.close()
+
+
+def spectra_info(c: Container) -> dict:
+    out = spectra_info_t()
+    _check(lib().spectra_info(c.handle, ctypes.byref(out)))
+    return {name: getattr(out, name) for name, _ in spectra_info_t._fields_}
+
+
+def spectra_export(c: Container) -> bytes:
+    total = c.info()["bytes_total"]
+    buf = (ctypes.c_ubyte * total)()
+    _check(lib().spectra_export(c.handle, buf, total))
+    return bytes(buf)
+
+
+def spectra_version() -> int:
+    return lib().spectra_version()

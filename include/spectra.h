@@ -174,9 +174,10 @@ int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t 
 int spectra_gemm_grouped(const spectra_container* const* cs, int count, const void* x,
                          void* const* ys, int64_t M, void* stream);
 
-/* Release the container and its device memory.  NULL-safe.  The handle is
- * poisoned first, so a later call with it returns SPECTRA_E_INVAL rather than
- * touching freed memory (as long as the host memory was not reused). */
+/* Release the container and its device memory.  NULL-safe; freeing a handle
+ * twice, or one this library did not return, does nothing.  Handles are
+ * checked against the library's set of live containers, so any later call
+ * with a freed handle returns SPECTRA_E_INVAL without dereferencing it. */
 void spectra_free(spectra_container* c);
 
 /* Shape and byte counts of a container. */

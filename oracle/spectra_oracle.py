@@ -212,7 +212,8 @@ def decode_codes(words: np.ndarray) -> np.ndarray:
     return q
 
 
-def pack(W16: np.ndarray, gamma16: np.ndarray, mask: np.ndarray | None = None) -> bytes:
+def pack(W16: np.ndarray, gamma16: np.ndarray, mask: np.ndarray | None = None,
+         row_block: int = 8192) -> bytes:
     """Build the full container image for W (fp16 [N][K]) and gamma (fp16 [K]).
 
     `mask` overrides the kurtosis decision (used only to re-derive the rest of
@@ -231,10 +232,7 @@ def pack(W16: np.ndarray, gamma16: np.ndarray, mask: np.ndarray | None = None) -
     K_b = K - n_out
     G = -(-K_b // GROUP)
 
-    Wb = W16[:, perm[:K_b]].astype(np.float64)
-    q, z, s16 = quantize_groups(Wb)
     O = W16[:, perm[K_b:]]
-
     off = layout(K, N, n_out)
     img = bytearray(off["total"])
     hdr = np.zeros(HEADER_BYTES // 8, dtype=np.uint64)
@@ -249,11 +247,14 @@ def pack(W16: np.ndarray, gamma16: np.ndarray, mask: np.ndarray | None = None) -
         mwords[k // 32] |= np.uint32(1) << np.uint32(k % 32)
     _put(img, off["mask"], mwords.astype("<u4"))
     _put(img, off["perm"], perm.astype("<i4"))
-    _put(img, off["codes"], encode_codes(q).astype("<u4"))
-    _put(img, off["scales"], s16.astype("<f2"))
-    zf = z.reshape(-1).astype(np.uint8)
-    if zf.size % 2:
-        zf = np.concatenate([zf, np.zeros(1, np.uint8)])
+    # Groups are independent, so rows are quantized in blocks only to bound memory.
+    zf = np.zeros(N * G + (N * G) % 2, dtype=np.uint8)
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        q, z, s16 = quantize_groups(W16[r0:r1][:, perm[:K_b]].astype(np.float64))
+        _put(img, off["codes"] + 16 * r0 * G, encode_codes(q).astype("<u4"))
+        _put(img, off["scales"] + 2 * r0 * G, s16.astype("<f2"))
+        zf[r0 * G:r1 * G] = z.reshape(-1)
     _put(img, off["zeros"], (zf[0::2] | (zf[1::2] << 4)).astype(np.uint8))
     _put(img, off["outliers"], O.astype("<f2"))
     return bytes(img)

@@ -1,0 +1,260 @@
+"""GPU parity of libspectra against the CPU oracle, through the C ABI.
+
+Packing must be bit-exact (the whole container image); products must meet
+|y - y_ref| <= 1e-3 * (|W_hat| |x|)[m][n] + 1e-6 per element, with y_ref the
+oracle's float64 product of the oracle's own reconstruction.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from dequant_gemv_spectra_amd import synth
+from oracle import spectra_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _sp():
+    from dequant_gemv_spectra_amd import spectra
+    return spectra
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def borderline(W, g, eps=1e-9):
+    kap, m2 = O.channel_kurtosis(W, g)
+    return np.nonzero((m2 > 0) & (np.abs(np.nan_to_num(kap, nan=0.0) - 3.0) < eps))[0]
+
+
+def oracle_image_for(W, g, gpu_img):
+    """Oracle image; where a channel's kurtosis is within rounding of 3.0 both
+    decisions are valid, so the oracle follows the GPU's decision there."""
+    mask = O.outlier_mask(W, g)
+    bl = borderline(W, g)
+    if bl.size:
+        gmask = O.unpack(gpu_img)["mask"]
+        ok = np.ones(mask.size, bool)
+        ok[bl] = False
+        assert np.array_equal(mask[ok], gmask[ok])
+        mask = mask.copy()
+        mask[bl] = gmask[bl]
+    return O.pack(W, g, mask=mask)
+
+
+def first_diff(a: bytes, b: bytes, ref_img: bytes):
+    hdr = np.frombuffer(ref_img, "<u8", 16)
+    names = ["mask", "perm", "codes", "scales", "zeros", "outliers", "total"]
+    offs = [int(v) for v in hdr[6:13]]
+    aa = np.frombuffer(a, np.uint8)
+    bb = np.frombuffer(b, np.uint8)
+    n = min(aa.size, bb.size)
+    idx = np.nonzero(aa[:n] != bb[:n])[0]
+    if idx.size == 0:
+        return f"sizes {len(a)} vs {len(b)}"
+    i = int(idx[0])
+    sec = "header"
+    for nm, o in zip(names, offs):
+        if i >= o:
+            sec = nm
+    return f"{idx.size} bytes differ; first at {i} (section {sec}): gpu {aa[i]:#x} oracle {bb[i]:#x}"
+
+
+def check_pack(W, g, device_input=False):
+    sp, torch = _sp(), _torch()
+    if device_input:
+        c = sp.spectra_pack(torch.from_numpy(W).cuda(), torch.from_numpy(g).cuda())
+    else:
+        c = sp.spectra_pack(W, g)
+    img = sp.spectra_export(c)
+    ref = oracle_image_for(W, g, img)
+    assert img == ref, first_diff(img, ref, ref)
+    return c, img
+
+
+def check_product(c, img, x, kernel="auto", rows=None):
+    sp, torch = _sp(), _torch()
+    y = sp.spectra_gemm(c, torch.from_numpy(x).cuda(), kernel=kernel)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    if rows is None:
+        W_hat = O.unpack(img)["W_hat"]
+        yr = O.matmul_ref(W_hat, x)
+        tol = O.tolerance(W_hat, x)
+        err = np.abs(y - yr)
+    else:
+        W_hat = O.reconstruct_rows(img, rows)
+        yr = O.matmul_ref(W_hat, x)
+        tol = O.tolerance(W_hat, x)
+        err = np.abs(y[:, rows] - yr)
+    bad = err > tol
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} outside tolerance; worst ratio "
+                           f"{(err / tol).max():.3g}")
+    return y
+
+
+SMALL = [  # (N, K, planted heavy-tailed channels, seed)
+    (1, 1, 0, 0), (2, 5, 0, 1), (3, 31, 1, 2), (17, 33, 2, 3), (64, 200, 9, 4),
+    (40, 64, 0, 5), (9, 97, 5, 6), (300, 1000, 10, 7), (129, 2088, 40, 8),
+    (1000, 96, 3, 9), (5, 4096, 40, 10), (257, 512, 0, 11), (33, 8192, 82, 12),
+    (700, 2560, 30, 13), (64, 9728, 120, 14), (2049, 1536, 15, 15),
+]
+
+
+@pytest.mark.parametrize("N,K,n_out,seed", SMALL)
+def test_pack_bitexact_and_product_small(N, K, n_out, seed):
+    W, g, x = synth.random_case(N, K, n_out, seed)
+    c, img = check_pack(W, g, device_input=(seed % 2 == 1))
+    check_product(c, img, x)
+
+
+def test_golden_container_on_gpu():
+    sp = _sp()
+    W = np.zeros((8, 3), dtype=np.float16)
+    W[0, 0] = 1.0
+    n = np.arange(8)
+    W[:, 1] = (-n / 16.0).astype(np.float16)
+    W[0, 1] = 0.0
+    W[:, 2] = ((15 - n) / 16.0).astype(np.float16)
+    c = sp.spectra_pack(W, np.ones(3, np.float16))
+    img = sp.spectra_export(c)
+    ref = O.pack(W, np.ones(3, np.float16))
+    assert img == ref, first_diff(img, ref, ref)
+
+
+def test_scale_rounding_ties_to_even():
+    # (hi - lo)/15 lands exactly halfway between two fp16 values: 1 + 2^-11 rounds
+    # down to 1 (even), 1 + 3*2^-11 rounds up to 1 + 2^-9 (even).
+    W = np.zeros((4, 32), np.float16)
+    W[0, 0], W[0, 1] = 15.0, -15 * 2.0 ** -11
+    W[1, 0], W[1, 1] = 15.0, -45 * 2.0 ** -11
+    W[2, 0], W[2, 1] = 7.5, -15 * 2.0 ** -12
+    W[3, 0], W[3, 1] = -3.0, 2.0 ** -14
+    g = np.ones(32, np.float16)
+    c, img = check_pack(W, g)
+    s16 = O.unpack(img)["s16"]
+    assert float(s16[0, 0]) == 1.0 and float(s16[1, 0]) == 1.0 + 2.0 ** -9
+
+
+def test_all_heavy_tailed_channels():
+    W = np.zeros((9, 5), np.float16)
+    for k in range(5):
+        W[k, k] = 1.0 + k
+    c, img = check_pack(W, np.ones(5, np.float16))
+    assert O.unpack(img)["G"] == 0
+    x = np.random.default_rng(0).standard_normal((1, 5)).astype(np.float16)
+    check_product(c, img, x)
+
+
+def test_one_hot_columns_exact():
+    sp, torch = _sp(), _torch()
+    W, g, _ = synth.random_case(333, 300, 6, 21)
+    c, img = check_pack(W, g)
+    u = O.unpack(img)
+    for k in list(u["perm"][u["K_b"]:][:4]) + [int(u["perm"][0]), int(u["perm"][37]),
+                                                int(u["perm"][u["K_b"] - 1])]:
+        x = np.zeros((1, 300), np.float16)
+        x[0, k] = 1.0
+        y = sp.spectra_gemm(c, torch.from_numpy(x).cuda()).cpu().numpy()[0]
+        expect = u["W_hat"][:, k].astype(np.float16)   # exact value, rounded once
+        assert np.array_equal(y, expect), k
+
+
+def test_output_canary_and_repeatability():
+    sp, torch = _sp(), _torch()
+    W, g, x = synth.random_case(1000, 777, 8, 22)
+    c, img = check_pack(W, g)
+    buf = torch.full((1, 1000 + 256), 12345.0, dtype=torch.float16, device="cuda")
+    ybig = buf[:, :1000]
+    xs = torch.from_numpy(x).cuda()
+    from dequant_gemv_spectra_amd.spectra import lib
+    import ctypes
+    rc = lib().spectra_gemm_ex(c.handle, ctypes.c_void_p(xs.data_ptr()), ctypes.c_void_p(ybig.data_ptr()),
+                               1, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), 0)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.all(buf[0, 1000:] == 12345.0)
+    y1 = buf[:, :1000].clone()
+    y2 = sp.spectra_gemm(c, xs)
+    assert torch.equal(y1, y2)
+    c2 = sp.spectra_pack(W, g)
+    assert sp.spectra_export(c2) == img
+
+
+def test_error_paths():
+    sp, torch = _sp(), _torch()
+    W, g, x = synth.random_case(64, 100, 2, 23)
+    c = sp.spectra_pack(W, g)
+    from dequant_gemv_spectra_amd.spectra import lib, SpectraError
+    import ctypes
+    L = lib()
+    xs = torch.from_numpy(x).cuda()
+    y = torch.empty((1, 64), dtype=torch.float16, device="cuda")
+    raw = torch.empty(64 + 8, dtype=torch.float16, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
+    assert L.spectra_gemm_ex(c.handle, P(xs.data_ptr()), P(raw.data_ptr() + 2), 1, st, 0) == sp.SPECTRA_E_INVAL
+    assert L.spectra_gemm_ex(c.handle, P(xs.data_ptr()), P(y.data_ptr()), 0, st, 0) == sp.SPECTRA_E_INVAL
+    assert L.spectra_gemm_ex(c.handle, None, P(y.data_ptr()), 1, st, 0) == sp.SPECTRA_E_INVAL
+    assert L.spectra_gemm_ex(c.handle, P(xs.data_ptr()), P(y.data_ptr()), 1, st, 7) == sp.SPECTRA_E_INVAL
+    assert L.spectra_gemm_ex(P(12345), P(xs.data_ptr()), P(y.data_ptr()), 1, st, 0) == sp.SPECTRA_E_INVAL
+    h = c.handle
+    c.close()
+    assert L.spectra_gemm_ex(h, P(xs.data_ptr()), P(y.data_ptr()), 1, st, 0) == sp.SPECTRA_E_INVAL
+    L.spectra_free(h)  # double free is a no-op
+    Wbad = W.copy()
+    Wbad[3, 7] = np.inf
+    with pytest.raises(SpectraError) as ei:
+        sp.spectra_pack(Wbad, g)
+    assert ei.value.status == sp.SPECTRA_E_NONFINITE
+    gbad = g.copy()
+    gbad[0] = np.nan
+    with pytest.raises(SpectraError):
+        sp.spectra_pack(W, gbad)
+    assert not L.spectra_pack(None, None, 4, 4)
+    assert not L.spectra_pack(W.ctypes.data_as(P), g.ctypes.data_as(P), 0, 4)
+
+
+def _linear_case(lin, cfg, M=1):
+    return synth.weights(lin, cfg), synth.gamma(lin, cfg), synth.activations(lin, cfg, M)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_config_full(cfg):
+    wl = synth.workload(cfg)
+    for lin in wl.linears:
+        W, g, x = _linear_case(lin, cfg)
+        c, img = check_pack(W, g)
+        check_product(c, img, x)
+        c.close()
+
+
+@pytest.mark.timeout(900)
+def test_config3_sampled_layers():
+    wl = synth.workload(3)
+    for lin in wl.linears:
+        if lin.layer not in (0, 35):
+            continue
+        W, g, x = _linear_case(lin, 3)
+        c, img = check_pack(W, g)
+        rows = np.random.default_rng(lin.lin_id).choice(lin.N, 256, replace=False)
+        check_product(c, img, x, rows=np.sort(rows))
+        c.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_config_large(cfg):
+    wl = synth.workload(cfg)
+    lin = wl.linears[0]
+    W, g, x = _linear_case(lin, cfg)
+    c, img = check_pack(W, g)
+    del W
+    rows = np.sort(np.random.default_rng(cfg).choice(lin.N, 2048, replace=False))
+    check_product(c, img, x, rows=rows)
