@@ -3,32 +3,71 @@
 // The SPECTRA page (abstract; highlight 4 on its fused kernels) describes
 // dequantization fused into the product so that only the packed weights cross
 // DRAM; the decode product is bound by weight bytes (the techfi24 summary,
-// "Contexte materiel": every token re-reads all weights).  This kernel is a
-// gfx950 design of that idea, not a port: the page's kernels target a laptop
-// Ampere GPU.
+// section on the hardware context: every token re-reads all weights).  This
+// kernel is a gfx950 design of that idea, not a port: the page's kernels
+// target a laptop Ampere GPU.
 //
 // Mapping.  A team of L lanes (L = 16, 32 or 64) owns one output row at a
 // time; lane t of a team owns the groups g = t + L*p (p < P) of every row it
-// visits, so each of its x slices (32 fp16 values per group) is loaded from
-// LDS into registers once per block and reused for every row.  A team's loads
-// for slot p cover 16*L contiguous bytes of codes (global_load_dwordx4 per
-// lane).  Each block stages x in bulk order (gathered through perm, padded
-// with zeros) plus the heavy-tailed x values in LDS, then walks its rows.
+// visits, so a team's load for slot p covers 16*L contiguous bytes of codes
+// (buffer_load_dwordx4 per lane).  A tile is T*U rows (T teams per block, U
+// rows per team); a block walks the tiles b, b + B, b + 2B, ... of its
+// container, so at any moment all blocks stream one moving window of HBM.
+// Two register buffers hold consecutive tiles: the next tile's loads are in
+// flight while the current one is computed.  Loads go through buffer
+// descriptors rebased on each tile, so rows past N and idle lanes read zeros
+// from the hardware range check with no branches.  One launch may carry up to
+// eight containers that share x (q/k/v or gate/up of a decoder layer).
 //
-// Arithmetic.  A code word w yields two members per 16-bit half with
-// (w >> 4i) & 0x000F000F; OR-ing 0x6400 into each half makes the fp16 values
-// 1024 + q exactly, and subtracting the fp16 pair (1024 + z) gives q - z
-// exactly.  v_dot2_f32_f16 multiplies by the matching x pair and accumulates
-// in fp32; the group sum is scaled by s16 in fp32.  The heavy-tailed columns
-// are a dense fp16 side product in the same pass.  Team partials are reduced
-// with DPP inside 16-lane rows and lane swizzles across rows.
+// Staging.  Each block copies x into LDS and gathers it into bulk order
+// through perm: x and perm are fetched with 16-byte loads in one round trip,
+// after the block has requested its first tile of weights.  In LDS each group's 32 halves occupy an 80-byte slot, which keeps
+// the per-lane 16-byte reads free of bank conflicts.
+//
+// Arithmetic.  For a code word w, (w & 0x000F000F) | 0x6400_6400 holds the
+// fp16 values 1024 + q of members (8d, 8d+1); (w & 0x00F000F0) | 0x6400_6400
+// holds 1024 + 16q of members (8d+2, 8d+3); the same two masks on w >> 8 give
+// members (8d+4, 8d+5) and (8d+6, 8d+7).  Subtracting the fp16 pairs
+// 1024 + z and 1024 + 16z leaves q - z and 16(q - z), both exact.
+// v_dot2_f32_f16 multiplies them by the matching x pairs and accumulates in
+// fp32 (two accumulators; the second is scaled by 1/16 exactly).  The group
+// sum is scaled by s16 in fp32.  The heavy-tailed columns are a dense fp16
+// side product in the same pass.  Team partials are reduced with DPP inside
+// 16-lane rows and lane swizzles across rows.
 #include "spectra_internal.h"
+
+#ifndef SPECTRA_GEMV_BLOCKS_PER_CU
+#define SPECTRA_GEMV_BLOCKS_PER_CU 2
+#endif
+#ifndef SPECTRA_GEMV_U
+#define SPECTRA_GEMV_U 1
+#endif
 
 namespace spectra {
 namespace {
 
-constexpr int kBlock = 256;
+#ifndef SPECTRA_GEMV_BLOCK
+#define SPECTRA_GEMV_BLOCK 256
+#endif
+constexpr int kBlock = SPECTRA_GEMV_BLOCK;
+constexpr int kWaves = kBlock / 64;
+constexpr int kMaxTasks = 8;
+constexpr int kXSlot = 40;  // halves per group slot in LDS (32 used, 80 bytes)
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct GemvTask {
+  DeviceView v;
+  const uint16_t* x;
+  uint16_t* y;
+  int32_t block_begin;  // first block of this task in the grid
+  int32_t nblocks;      // blocks serving this task
+};
+
+struct GemvTasks {
+  GemvTask t[kMaxTasks];
+  int32_t count;
+};
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -56,110 +95,252 @@ __device__ __forceinline__ uint16_t f2h(float f) {
 }
 __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
-// Dot of one 16-byte code record (32 members) with the matching 16 x pairs,
-// zero point folded in exactly.  Returns sum_e (q_e - z) * x_e in fp32.
-__device__ __forceinline__ float group_dot(const uint4 c, const uint32_t z, const half2_t* xr) {
-  const half2_t zp = as_h2((0x6400u + z) * 0x00010001u);
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float t = 0.f;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const half2_t q = as_h2(((w[d] >> (4 * i)) & 0x000F000Fu) | 0x64006400u);
-      t = __builtin_amdgcn_fdot2(q - zp, xr[4 * d + i], t, false);
-    }
-  }
-  return t;
+// Buffer descriptors (gfx9 raw buffer, stride 0): the hardware range check
+// returns 0 for any byte offset at or past num_records, so loads need no
+// branches.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every descriptor built here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_t bytes) {
+  const int n = bytes >= 0x7FFFFFFFull ? 0x7FFFFFFF : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
 }
 
-template <int L, int P, int U>
-__global__ __launch_bounds__(kBlock) void k_gemv_m1(DeviceView v, const uint16_t* __restrict__ x,
-                                                    uint16_t* __restrict__ y,
-                                                    int64_t rows_per_block) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int T = kBlock / L;  // teams per block
-  const int G = v.G, K_b = v.K_b, n_out = v.n_out;
-  const int xs_bytes = (64 * G + 15) & ~15;
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* xo = reinterpret_cast<float*>(smem + xs_bytes);
-  const int tid = threadIdx.x;
+// (a & m) | o in one VALU op (VOP3 on gfx9 takes no literal, so the compiler
+// otherwise splits it into an AND and an OR with literals).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+  return r;
+}
 
-  // Stage x (bulk order, zero padded to 32G) and the heavy-tailed x values.
-  for (int j = tid; j < 32 * G; j += kBlock) xs[j] = (j < K_b) ? x[v.perm[j]] : (uint16_t)0;
-  for (int j = tid; j < n_out; j += kBlock) xo[j] = h2f(x[v.perm[K_b + j]]);
+// sum_e (q_e - z) * x_e over one 16-byte code record, in fp32.
+__device__ __forceinline__ float group_dot(const uint4 c, const uint32_t z, const half2_t* xr) {
+  constexpr uint32_t kLo = 0x000F000Fu, kHi = 0x00F000F0u, kMagic = 0x64006400u;
+  const half2_t zp = as_h2((0x6400u + z) * 0x00010001u);          // 1024 + z
+  const half2_t zp16 = as_h2((0x6400u + 16u * z) * 0x00010001u);  // 1024 + 16 z
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float ta = 0.f, tb = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t w8 = w[d] >> 8;
+    ta = __builtin_amdgcn_fdot2(as_h2(and_or(w[d], kLo, kMagic)) - zp, xr[4 * d + 0], ta, false);
+    tb = __builtin_amdgcn_fdot2(as_h2(and_or(w[d], kHi, kMagic)) - zp16, xr[4 * d + 1], tb, false);
+    ta = __builtin_amdgcn_fdot2(as_h2(and_or(w8, kLo, kMagic)) - zp, xr[4 * d + 2], ta, false);
+    tb = __builtin_amdgcn_fdot2(as_h2(and_or(w8, kHi, kMagic)) - zp16, xr[4 * d + 3], tb, false);
+  }
+  return __builtin_fmaf(tb, 0.0625f, ta);
+}
+
+__device__ __forceinline__ int xs_index(int j) { return (j >> 5) * kXSlot + (j & 31); }
+
+// Gather x into LDS: bulk positions [0, K_b) in their 80-byte group slots,
+// zeros up to 32G, then the heavy-tailed values (fp16) right after the slots.
+//   A. One round trip: each thread issues 16-byte loads of x (8 channels) and
+//      of perm (4 bulk positions), plus the perm entry of one heavy-tailed
+//      channel.
+//   B. x is written to LDS as is (`xraw`, channel order); barrier.
+//   C. Each thread reads its 4 positions' values from xraw through the perm
+//      entries and stores them as one 8-byte write into the group slot.
+// Positions past K_b, and channels past K, read zero through the range check
+// of the buffer descriptors.
+constexpr int kQuads = 12;  // perm quads per thread per pass: 12288 positions
+constexpr int kXChunks = 6; // 8-channel x chunks per thread per pass: 12288 channels
+__device__ void stage_x(const DeviceView& v, const uint16_t* __restrict__ x, uint16_t* xs,
+                        uint16_t* xraw, int tid) {
+  const int K = v.K, K_b = v.K_b, n_out = v.n_out;
+  const int xo_base = kXSlot * v.G;  // heavy-tailed x (fp16) follow the group slots
+  const int nquad = 8 * v.G;         // 32G / 4
+  const int nchunk = (K + 7) >> 3;
+  const __amdgpu_buffer_rsrc_t rp = rsrc(v.perm, (uint64_t)K * 4);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, (uint64_t)(K >> 3) * 16);  // whole chunks only
+  // A. loads
+  const uint32_t oidx = __builtin_amdgcn_raw_buffer_load_b32(
+      rp, tid < n_out ? (uint32_t)(K_b + tid) * 4u : kOob, 0, 0);
+  u32x4 xv[kXChunks];
+#pragma unroll
+  for (int i = 0; i < kXChunks; ++i) {
+    if (kBlock * i >= nchunk) break;  // block-uniform bound
+    xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(tid + kBlock * i) * 16u, 0, 0);
+  }
+  u32x4 pq[kQuads];
+#pragma unroll
+  for (int i = 0; i < kQuads; ++i) {
+    if (kBlock * i >= nquad) break;
+    pq[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)(tid + kBlock * i) * 16u, 0, 0);
+  }
+  // B. raw x into LDS (a partial last chunk is read channel by channel)
+#pragma unroll
+  for (int i = 0; i < kXChunks; ++i) {
+    if (kBlock * i >= nchunk) break;
+    const int c = tid + kBlock * i;
+    if (c < nchunk) {
+      u32x4 t = xv[i];
+      if (8 * c + 8 > K) {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = 8 * c + e < K ? x[8 * c + e] : 0u;
+        t = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      }
+      *reinterpret_cast<u32x4*>(xraw + 8 * c) = t;
+    }
+  }
   __syncthreads();
+  // C. gather from xraw into the group slots
+#pragma unroll
+  for (int i = 0; i < kQuads; ++i) {
+    if (kBlock * i >= nquad) break;
+    const int c = tid + kBlock * i;
+    const int j = 4 * c;
+    const uint32_t a0 = j + 0 < K_b ? xraw[pq[i].x] : 0u;
+    const uint32_t a1 = j + 1 < K_b ? xraw[pq[i].y] : 0u;
+    const uint32_t a2 = j + 2 < K_b ? xraw[pq[i].z] : 0u;
+    const uint32_t a3 = j + 3 < K_b ? xraw[pq[i].w] : 0u;
+    if (c < nquad)
+      *reinterpret_cast<uint2*>(xs + xs_index(j)) = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+  }
+  if (tid < n_out) xs[xo_base + tid] = xraw[oidx];
+  for (int j = tid + kBlock; j < n_out; j += kBlock) xs[xo_base + j] = xraw[v.perm[K_b + j]];
+}
 
-  const int lt = tid % L;
-  const int team = tid / L;
-  half2_t xr[P][16];
+// Registers holding one tile of weights for a lane: U rows x P groups of
+// codes, scale bits | zero byte << 16, and OS heavy-tailed weights per row.
+template <int P, int U, int OS>
+struct Frag {
+  uint4 c[U][P];
+  uint32_t sz[U][P];
+  uint32_t o[U][OS];
+};
+
+// Loads the tile whose first row is row0 (rows >= N read as zero).  The
+// descriptors are rebased on the tile so offsets stay small for any size.
+template <int L, int P, int U, int OS>
+__device__ __forceinline__ void load_frag(Frag<P, U, OS>& f, const DeviceView& v, int64_t row0,
+                                          int lt, int team) {
+  constexpr int T = kBlock / L;
+  const int G = v.G, n_out = v.n_out;
+  const int64_t left = v.N - row0;
+  const int64_t rows = left < (int64_t)T * U ? (left > 0 ? left : 0) : (int64_t)T * U;
+  const int64_t i0 = row0 * G;  // flat group index of the tile's first group
+  const __amdgpu_buffer_rsrc_t rc = rsrc(v.codes + i0, (uint64_t)rows * G * 16);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(v.scales + i0, (uint64_t)rows * G * 2);
+  const int64_t zb0 = i0 >> 1;
+  const __amdgpu_buffer_rsrc_t rz = rsrc(v.zeros + zb0, (uint64_t)(((i0 + rows * G + 1) >> 1) - zb0));
+  const __amdgpu_buffer_rsrc_t ro = rsrc(v.outliers + row0 * n_out, (uint64_t)rows * n_out * 2);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int row = team + u * T;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int g = lt + L * p;
+      const uint32_t local = (uint32_t)(row * G + g);
+      const bool ok = g < G;
+      const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? local * 16u : kOob, 0, 0);
+      f.c[u][p] = make_uint4(c.x, c.y, c.z, c.w);
+      const uint32_t s = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? local * 2u : kOob, 0, 0);
+      const uint32_t zoff = (uint32_t)(((i0 + local) >> 1) - zb0);
+      const uint32_t z = __builtin_amdgcn_raw_buffer_load_b8(rz, ok ? zoff : kOob, 0, 0);
+      f.sz[u][p] = s | (z << 16);
+    }
+#pragma unroll
+    for (int s = 0; s < OS; ++s) {
+      const int j = lt + L * s;
+      const uint32_t off = (uint32_t)(row * n_out + j) * 2u;
+      f.o[u][s] = __builtin_amdgcn_raw_buffer_load_b16(ro, j < n_out ? off : kOob, 0, 0);
+    }
+  }
+}
+
+template <int L, int P, int U, int OS>
+__device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const DeviceView& v,
+                                             int64_t row0, int lt, int team, const uint16_t* xs,
+                                             const float* xor_, const uint16_t* xo,
+                                             uint16_t* __restrict__ y) {
+  constexpr int T = kBlock / L;
+  const int G = v.G, n_out = v.n_out;
+  float acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = 0.f;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int g = lt + L * p;
-    if (g < G) {
-      const uint4* src = reinterpret_cast<const uint4*>(xs + 32 * g);
+    half2_t xr[16];
+    const uint4* src = reinterpret_cast<const uint4*>(xs + (g < G ? g : 0) * kXSlot);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 u = src[q];
-        xr[p][4 * q + 0] = as_h2(u.x);
-        xr[p][4 * q + 1] = as_h2(u.y);
-        xr[p][4 * q + 2] = as_h2(u.z);
-        xr[p][4 * q + 3] = as_h2(u.w);
-      }
-    } else {
+    for (int q = 0; q < 4; ++q) {
+      const uint4 t = src[q];
+      xr[4 * q + 0] = as_h2(t.x);
+      xr[4 * q + 1] = as_h2(t.y);
+      xr[4 * q + 2] = as_h2(t.z);
+      xr[4 * q + 3] = as_h2(t.w);
+    }
 #pragma unroll
-      for (int q = 0; q < 16; ++q) xr[p][q] = as_h2(0u);
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = (row0 + team + (int64_t)u * T) * G + g;
+      const uint32_t z = (f.sz[u][p] >> (16u + 4u * (uint32_t)(i & 1))) & 0xFu;
+      acc[u] = __builtin_fmaf(h2f((uint16_t)f.sz[u][p]), group_dot(f.c[u][p], z, xr), acc[u]);
     }
   }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t n = row0 + team + (int64_t)u * T;
+    float a = acc[u];
+#pragma unroll
+    for (int s = 0; s < OS; ++s) a = __builtin_fmaf(xor_[s], h2f((uint16_t)f.o[u][s]), a);
+    if (n < v.N && n_out > L * OS) {  // heavy-tailed columns beyond the register slots
+      const uint16_t* orow = v.outliers + n * n_out;
+      for (int j = lt + L * OS; j < n_out; j += L) a = __builtin_fmaf(h2f(xo[j]), h2f(orow[j]), a);
+    }
+    const float s = team_sum<L>(a);
+    if (lt == 0 && n < v.N) y[n] = f2h(s);
+  }
+}
 
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
-  const int64_t r1 = (r0 + rows_per_block < v.N) ? r0 + rows_per_block : v.N;
-  for (int64_t tile = r0; tile < r1; tile += (int64_t)T * U) {
-    uint4 c[U][P];
-    uint16_t sc[U][P];
-    uint8_t zb[U][P];
+template <int L, int P, int U>
+__global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
+  constexpr int OS = (L == 16) ? 4 : 2;  // heavy-tailed slots per lane held in registers
+  constexpr int T = kBlock / L;          // teams per block
+  constexpr int kTileRows = T * U;
+  extern __shared__ __align__(16) unsigned char smem[];
+  int ti = 0;
+  for (int i = 1; i < tasks.count; ++i)
+    if ((int32_t)blockIdx.x >= tasks.t[i].block_begin) ti = i;
+  const GemvTask& task = tasks.t[ti];
+  const DeviceView& v = task.v;
+  const int G = v.G, n_out = v.n_out;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  const uint16_t* xo = xs + kXSlot * G;
+  uint16_t* xraw = xs + (((kXSlot * G + n_out) + 7) & ~7);  // 16-byte aligned
+  const int tid = threadIdx.x;
+  const int lt = tid % L;
+  const int team = tid / L;
+  const int64_t stride = (int64_t)task.nblocks * kTileRows;
+  int64_t row = (int64_t)(blockIdx.x - task.block_begin) * kTileRows;
+
+  // The first tile's weights are requested before x is staged, so their HBM
+  // latency overlaps the gather and the barrier.
+  Frag<P, U, OS> fa, fb;
+  load_frag<L, P, U, OS>(fa, v, row, lt, team);
+  stage_x(v, task.x, xs, xraw, tid);
+  __syncthreads();
+
+  float xor_[OS];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t n = tile + team + (int64_t)u * T;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int g = lt + L * p;
-        if (n < r1 && g < G) {
-          const int64_t i = n * G + g;
-          c[u][p] = v.codes[i];
-          sc[u][p] = v.scales[i];
-          zb[u][p] = v.zeros[i >> 1];
-        } else {
-          c[u][p] = make_uint4(0u, 0u, 0u, 0u);
-          sc[u][p] = 0;
-          zb[u][p] = 0;
-        }
-      }
-    }
-    float acc[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t n = tile + team + (int64_t)u * T;
-      float a = 0.f;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int g = lt + L * p;
-        const int64_t i = n * G + g;
-        const uint32_t z = ((uint32_t)zb[u][p] >> ((uint32_t)(i & 1) * 4u)) & 0xFu;
-        a = __builtin_fmaf(h2f(sc[u][p]), group_dot(c[u][p], z, xr[p]), a);
-      }
-      if (n < r1) {
-        const uint16_t* orow = v.outliers + n * n_out;
-        for (int j = lt; j < n_out; j += L) a = __builtin_fmaf(xo[j], h2f(orow[j]), a);
-      }
-      acc[u] = a;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t n = tile + team + (int64_t)u * T;
-      const float s = team_sum<L>(acc[u]);
-      if (lt == 0 && n < r1) y[n] = f2h(s);
-    }
+  for (int s = 0; s < OS; ++s) {
+    const int j = lt + L * s;
+    xor_[s] = j < n_out ? h2f(xo[j]) : 0.f;
+  }
+  // Two register buffers, unrolled by hand: the next tile is in flight while
+  // this one is computed.
+  for (;;) {
+    if (row >= v.N) break;
+    load_frag<L, P, U, OS>(fb, v, row + stride, lt, team);
+    compute_frag<L, P, U, OS>(fa, v, row, lt, team, xs, xor_, xo, task.y);
+    row += stride;
+    if (row >= v.N) break;
+    load_frag<L, P, U, OS>(fa, v, row + stride, lt, team);
+    compute_frag<L, P, U, OS>(fb, v, row, lt, team, xs, xor_, xo, task.y);
+    row += stride;
   }
 }
 
@@ -167,7 +348,8 @@ struct Variant {
   int L, P;
 };
 
-// Pick lanes-per-row L and slots-per-lane P = ceil(G/L) with the best lane use.
+// Lanes-per-row L and slots-per-lane P = ceil(G/L) with the best lane use
+// (ties: fewer slots, i.e. fewer registers).  P == 0: no variant fits.
 Variant pick_variant(int G) {
   Variant best{64, 0};
   double best_eff = -1.0;
@@ -185,65 +367,108 @@ Variant pick_variant(int G) {
   return best;
 }
 
-constexpr int kU = 2;
+size_t lds_bytes(const DeviceView& v) {
+  return 2 * ((((size_t)kXSlot * v.G + (size_t)v.n_out) + 7) & ~(size_t)7) +
+         16 * (((size_t)v.K + 7) / 8);
+}
+
+constexpr int kU = SPECTRA_GEMV_U;
+constexpr size_t kMaxLds = 64 * 1024;
+
+// Split the block budget between the tasks in proportion to their rows.
+template <int L>
+int64_t plan_blocks(GemvTasks& ts) {
+  constexpr int64_t kTileRows = (int64_t)(kBlock / L) * kU;
+  int64_t total_rows = 0;
+  for (int i = 0; i < ts.count; ++i) total_rows += ts.t[i].v.N;
+  const int64_t budget = (int64_t)ts.t[0].v.cu_count * SPECTRA_GEMV_BLOCKS_PER_CU;
+  int64_t begin = 0;
+  for (int i = 0; i < ts.count; ++i) {
+    GemvTask& t = ts.t[i];
+    const int64_t tiles = (t.v.N + kTileRows - 1) / kTileRows;
+    int64_t blocks = (budget * t.v.N + total_rows - 1) / total_rows;
+    if (blocks > tiles) blocks = tiles;
+    if (blocks < 1) blocks = 1;
+    t.block_begin = (int32_t)begin;
+    t.nblocks = (int32_t)blocks;
+    begin += blocks;
+  }
+  return begin;
+}
 
 template <int L, int P>
-hipError_t launch_lp(const DeviceView& v, const uint16_t* x, uint16_t* y, hipStream_t s) {
-  const int cu = v.cu_count;
-  constexpr int T = kBlock / L;
-  const int64_t rows_per_tile = (int64_t)T * kU;
-  const int64_t tiles = (v.N + rows_per_tile - 1) / rows_per_tile;
-  int64_t blocks = tiles < (int64_t)cu * 4 ? tiles : (int64_t)cu * 4;
-  if (blocks < 1) blocks = 1;
-  const int64_t tiles_per_block = (tiles + blocks - 1) / blocks;
-  const int64_t rows_per_block = tiles_per_block * rows_per_tile;
-  blocks = (v.N + rows_per_block - 1) / rows_per_block;
-  const size_t lds = (size_t)((64 * v.G + 15) & ~15) + 4 * (size_t)v.n_out;
-  hipLaunchKernelGGL((k_gemv_m1<L, P, kU>), dim3((unsigned)blocks), dim3(kBlock), lds, s, v, x, y,
-                     rows_per_block);
+hipError_t launch_lp(GemvTasks& ts, size_t lds, hipStream_t s) {
+  const int64_t blocks = plan_blocks<L>(ts);
+  hipLaunchKernelGGL((k_gemv_m1<L, P, kU>), dim3((unsigned)blocks), dim3(kBlock), lds, s, ts);
   return hipGetLastError();
 }
 
 template <int L>
-hipError_t launch_l(int P, const DeviceView& v, const uint16_t* x, uint16_t* y, hipStream_t s) {
+hipError_t launch_l(int P, GemvTasks& ts, size_t lds, hipStream_t s) {
   switch (P) {
-    case 1: return launch_lp<L, 1>(v, x, y, s);
-    case 2: return launch_lp<L, 2>(v, x, y, s);
-    case 3: return launch_lp<L, 3>(v, x, y, s);
-    case 4: return launch_lp<L, 4>(v, x, y, s);
-    case 5: return launch_lp<L, 5>(v, x, y, s);
-    case 6: return launch_lp<L, 6>(v, x, y, s);
-    case 7: return launch_lp<L, 7>(v, x, y, s);
-    case 8: return launch_lp<L, 8>(v, x, y, s);
+    case 1: return launch_lp<L, 1>(ts, lds, s);
+    case 2: return launch_lp<L, 2>(ts, lds, s);
+    case 3: return launch_lp<L, 3>(ts, lds, s);
+    case 4: return launch_lp<L, 4>(ts, lds, s);
+    case 5: return launch_lp<L, 5>(ts, lds, s);
+    case 6: return launch_lp<L, 6>(ts, lds, s);
+    case 7: return launch_lp<L, 7>(ts, lds, s);
+    case 8: return launch_lp<L, 8>(ts, lds, s);
     default: return hipErrorNotSupported;
   }
 }
 
-constexpr size_t kMaxLds = 64 * 1024;
+hipError_t launch_tasks(GemvTasks& ts, hipStream_t s) {
+  int gmax = 0;
+  size_t lds = 0;
+  for (int i = 0; i < ts.count; ++i) {
+    if (ts.t[i].v.G > gmax) gmax = ts.t[i].v.G;
+    const size_t b = lds_bytes(ts.t[i].v);
+    if (b > lds) lds = b;
+  }
+  const Variant vr = pick_variant(gmax);
+  if (vr.P == 0 || lds > kMaxLds) return hipErrorNotSupported;
+  switch (vr.L) {
+    case 16: return launch_l<16>(vr.P, ts, lds, s);
+    case 32: return launch_l<32>(vr.P, ts, lds, s);
+    default: return launch_l<64>(vr.P, ts, lds, s);
+  }
+}
 
 }  // namespace
 
 bool gemv_supports(const DeviceView& v, int64_t M) {
   if (M != 1) return false;
   if (pick_variant(v.G).P == 0) return false;
-  const size_t lds = (size_t)((64 * v.G + 15) & ~15) + 4 * (size_t)v.n_out;
-  return lds <= kMaxLds;
+  return lds_bytes(v) <= kMaxLds;
 }
 
 hipError_t launch_gemv(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M,
                        hipStream_t s) {
   if (!gemv_supports(v, M)) return hipErrorNotSupported;
-  const Variant vr = pick_variant(v.G);
-  switch (vr.L) {
-    case 16: return launch_l<16>(vr.P, v, x, y, s);
-    case 32: return launch_l<32>(vr.P, v, x, y, s);
-    default: return launch_l<64>(vr.P, v, x, y, s);
-  }
+  GemvTasks ts;
+  ts.count = 1;
+  ts.t[0].v = v;
+  ts.t[0].x = x;
+  ts.t[0].y = y;
+  return launch_tasks(ts, s);
 }
 
-hipError_t launch_gemv_grouped(const DeviceView*, int, const uint16_t*, uint16_t* const*,
-                               hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_gemv_grouped(const DeviceView* vs, int count, const uint16_t* x,
+                               uint16_t* const* ys, hipStream_t s) {
+  for (int base = 0; base < count; base += kMaxTasks) {
+    GemvTasks ts;
+    ts.count = (count - base < kMaxTasks) ? count - base : kMaxTasks;
+    for (int i = 0; i < ts.count; ++i) {
+      if (!gemv_supports(vs[base + i], 1)) return hipErrorNotSupported;
+      ts.t[i].v = vs[base + i];
+      ts.t[i].x = x;
+      ts.t[i].y = ys[base + i];
+    }
+    const hipError_t e = launch_tasks(ts, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace spectra

@@ -47,6 +47,7 @@ struct DeviceView {
   const uint8_t* zeros;      // [ceil(N*G/2)] nibbles
   const uint16_t* outliers;  // [N][n_out] fp16 bits
   const int32_t* perm;       // [K]
+  const uint32_t* mask;      // [ceil(K/32)] heavy-tailed channel bits
   int64_t N;
   int32_t K, K_b, G, n_out;
   int32_t cu_count;          // compute units of the container's device (launch sizing)
@@ -74,6 +75,7 @@ struct spectra_container {
     v.zeros = reinterpret_cast<const uint8_t*>(dev + lay.zeros);
     v.outliers = reinterpret_cast<const uint16_t*>(dev + lay.outliers);
     v.perm = reinterpret_cast<const int32_t*>(dev + lay.perm);
+    v.mask = reinterpret_cast<const uint32_t*>(dev + lay.mask);
     v.N = N;
     v.K = (int32_t)K;
     v.K_b = (int32_t)K_b;

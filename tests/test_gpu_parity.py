@@ -258,3 +258,22 @@ def test_config_large(cfg):
     del W
     rows = np.sort(np.random.default_rng(cfg).choice(lin.N, 2048, replace=False))
     check_product(c, img, x, rows=rows)
+
+
+def test_grouped_launch_matches_single_launches():
+    sp, torch = _sp(), _torch()
+    from dequant_gemv_spectra_amd import synth as S
+    cs, imgs = [], []
+    for i, (N, n_out) in enumerate([(1024, 30), (256, 12), (4096, 51), (333, 0)]):
+        W, g, _ = S.random_case(N, 2560, n_out, 40 + i)
+        c, img = check_pack(W, g)
+        cs.append(c)
+        imgs.append(img)
+    x = np.random.default_rng(5).standard_normal((1, 2560)).astype(np.float16)
+    xs = torch.from_numpy(x).cuda()
+    ys = sp.spectra_gemm_grouped(cs, xs)
+    for c, img, yg in zip(cs, imgs, ys):
+        y1 = sp.spectra_gemm(c, xs, kernel="gemv")
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y1)
+        check_product(c, img, x)
