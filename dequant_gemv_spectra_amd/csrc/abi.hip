@@ -5,9 +5,11 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
 #include <mutex>
 #include <new>
 #include <unordered_set>
+#include <utility>
 #include <vector>
 
 #include "../../include/spectra.h"
@@ -54,6 +56,40 @@ const DeviceProps& device_props(int device) {
     pc.have[device] = true;
   }
   return pc.props[device];
+}
+
+namespace {
+struct WorkspaceCache {
+  std::mutex mu;
+  std::map<std::pair<int, void*>, std::pair<void*, size_t>> bufs;
+};
+WorkspaceCache& workspace_cache() {
+  static WorkspaceCache wc;
+  return wc;
+}
+}  // namespace
+
+hipError_t stream_workspace(int device, hipStream_t s, size_t bytes, void** out) {
+  WorkspaceCache& wc = workspace_cache();
+  std::lock_guard<std::mutex> lk(wc.mu);
+  auto& e = wc.bufs[std::make_pair(device, static_cast<void*>(s))];
+  if (e.first && e.second >= bytes) {
+    *out = e.first;
+    return hipSuccess;
+  }
+  hipError_t err;
+  if (e.first) {  // work already queued on s may still read the old buffer
+    if ((err = hipStreamSynchronize(s)) != hipSuccess) return err;
+    (void)hipFree(e.first);
+    e = std::make_pair(nullptr, (size_t)0);
+  }
+  size_t nb = bytes < 2 * e.second ? 2 * e.second : bytes;
+  if (nb < (1u << 20)) nb = 1u << 20;
+  void* p = nullptr;
+  if ((err = hipMalloc(&p, nb)) != hipSuccess) return err;
+  e = std::make_pair(p, nb);
+  *out = p;
+  return hipSuccess;
 }
 
 namespace {
@@ -309,7 +345,10 @@ int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t 
     e = launch_gemv(v, xp, yp, M, s);
   } else {
     if (!mfma_supports(v, M)) return fail(SPECTRA_E_UNSUPPORTED, "MFMA kernel cannot run this shape");
-    e = launch_mfma(v, xp, yp, M, s);
+    void* ws = nullptr;
+    e = stream_workspace(c->device, s, mfma_workspace_bytes(v, M), &ws);
+    if (e != hipSuccess) return fail(SPECTRA_E_NOMEM, hip_msg("MFMA workspace", e));
+    e = launch_mfma_ws(v, xp, yp, M, ws, s);
   }
   if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("kernel launch", e));
   return SPECTRA_OK;

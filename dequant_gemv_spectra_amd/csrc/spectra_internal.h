@@ -109,6 +109,14 @@ hipError_t launch_gemv(const DeviceView& v, const uint16_t* x, uint16_t* y, int6
 hipError_t launch_gemv_grouped(const DeviceView* vs, int count, const uint16_t* x,
                                uint16_t* const* ys, hipStream_t s);
 bool mfma_supports(const DeviceView& v, int64_t M);
-hipError_t launch_mfma(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M, hipStream_t s);
+// Device workspace the MFMA path needs for M input rows (x permuted to bulk order).
+size_t mfma_workspace_bytes(const DeviceView& v, int64_t M);
+hipError_t launch_mfma_ws(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M,
+                          void* workspace, hipStream_t s);
+
+// ---- per-stream workspace (abi.hip) ----
+// A device buffer of at least `bytes` reserved for work enqueued on stream s
+// of `device`; grown on demand (growth waits for s and reallocates).
+hipError_t stream_workspace(int device, hipStream_t s, size_t bytes, void** out);
 
 }  // namespace spectra

@@ -277,3 +277,56 @@ def test_grouped_launch_matches_single_launches():
         torch.cuda.synchronize()
         assert torch.equal(yg, y1)
         check_product(c, img, x)
+
+
+MFMA_CASES = [  # (N, K, planted heavy-tailed channels, seed, M)
+    (64, 200, 9, 31, 2), (100, 1000, 10, 32, 3), (129, 2088, 40, 33, 16), (300, 96, 3, 34, 17),
+    (65, 4096, 40, 35, 33), (257, 2560, 30, 36, 70), (128, 8192, 82, 37, 128), (77, 512, 0, 38, 130),
+    (33, 31, 1, 39, 5), (9, 5, 0, 40, 7),
+]
+
+
+@pytest.mark.parametrize("N,K,n_out,seed,M", MFMA_CASES)
+def test_mfma_product_small(N, K, n_out, seed, M):
+    W, g, x = synth.random_case(N, K, n_out, seed, M=M)
+    c, img = check_pack(W, g)
+    check_product(c, img, x)                   # auto: the MFMA path for M >= 2
+    check_product(c, img, x, kernel="mfma")
+
+
+def test_mfma_at_m1_and_gemv_agree_with_oracle():
+    W, g, x = synth.random_case(700, 2560, 30, 41, M=1)
+    c, img = check_pack(W, g)
+    check_product(c, img, x, kernel="mfma")
+    check_product(c, img, x, kernel="gemv")
+
+
+def test_mfma_one_hot_columns_exact():
+    sp, torch = _sp(), _torch()
+    W, g, _ = synth.random_case(200, 300, 6, 42)
+    W[:, 11] = (np.random.default_rng(2).standard_t(3, 200) * 0.2).astype(np.float16)
+    c, img = check_pack(W, g)
+    u = O.unpack(img)
+    ks = list(u["perm"][u["K_b"]:][:3]) + [int(u["perm"][0]), int(u["perm"][u["K_b"] - 1])]
+    x = np.zeros((len(ks), 300), np.float16)
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    y = sp.spectra_gemm(c, torch.from_numpy(x).cuda(), kernel="mfma").cpu().numpy()
+    for i, k in enumerate(ks):
+        assert np.array_equal(y[i], u["W_hat"][:, k].astype(np.float16)), k
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_config_large_batched(cfg):
+    wl = synth.workload(cfg)
+    lin = wl.linears[0]
+    W, g = synth.weights(lin, cfg), synth.gamma(lin, cfg)
+    c, img = check_pack(W, g)
+    del W
+    rows = np.sort(np.random.default_rng(cfg + 7).choice(lin.N, 1024, replace=False))
+    for M in wl.Ms:
+        if M == 1:
+            continue
+        x = synth.activations(lin, cfg, M)
+        check_product(c, img, x, rows=rows)
