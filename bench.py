@@ -1,48 +1,61 @@
 #!/usr/bin/env python3
 """SPECTRA dequant-GEMV benchmark on one MI355X: effective HBM GB/s.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg3] [--M 1]
 
-Default workload (cfg3): the decode step of a 4B-class decoder -- 36 layers x
-7 linears (q/k/v/o/gate/up/down, hidden 2560, MLP 9728), M = 1, every layer's
-weights distinct, so one step streams about 2.2 GB of packed weights from HBM.
-Same-input projections run as one grouped launch (q/k/v, gate/up): 4 launches
-per layer.  One step = one pass over all 36 layers.  Inputs (containers and
-x) are resident in HBM before the timed region.
+Default workload (cfg3): the M = 1 decode step of a 4B-class decoder -- 36
+layers x 7 linears (q/k/v/o/gate/up/down, hidden 2560, MLP 9728), every layer
+distinct, so one step streams about 2.2 GB of packed weights from HBM.
+Same-input projections run as one grouped launch (q/k/v and gate/up): 4
+launches per layer, 144 per step, replayed as one captured HIP graph.
+Containers and inputs are resident in HBM before timing starts.
 
-value = algorithmic bytes per step / step time, where a linear's algorithmic
-bytes are its container payload (codes + scales + zero nibbles + fp16
-heavy-tailed columns) + metadata (header, mask, perm) + x + y, each counted
-once.  Prints ONE JSON line.
+value = algorithmic bytes per step / step time.  A linear's algorithmic bytes
+are its container payload (codes + scales + zero nibbles + fp16 heavy-tailed
+columns) + metadata (header, mask, perm) + x + y, each counted once (a
+grouped launch counts x once).
 
-Other workloads (--workload cfg1|cfg2|cfg4|cfg5, --M m) measure one linear (or
-one decoder layer) rotated over enough distinct copies to exceed 1 GiB so the
-last-level cache cannot serve the weights.
+Other workloads: cfg1 / cfg4 / cfg5 time one linear per step, rotating over
+enough distinct packed copies to exceed 1 GiB so the last-level cache cannot
+serve the weights; cfg2 stacks the 1.5B-class layer 28 deep.
+
+Prints ONE JSON line.  roofline: the dominant kernel (largest share of step
+bytes) is replayed alone as a captured graph and timed with HIP events on its
+launch stream; achieved = its algorithmic bytes per launch / average launch
+time; traffic comes from a committed counter profile when it matches the
+current kernel source.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "dequant-GEMV effective HBM GB/s and % of peak at M=1; weights-GB/s vs M"
-PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
+PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
+PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="cfg3", choices=["cfg1", "cfg2", "cfg3", "cfg4", "cfg5"])
     ap.add_argument("--M", type=int, default=1)
     ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "mfma"])
-    ap.add_argument("--layers", type=int, default=None, help="cfg3 only: fewer layers (smoke runs)")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a hipGraph")
+    ap.add_argument("--layers", type=int, default=None, help="cfg3: fewer layers (quick runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every unit directly instead of replaying graphs (for counter runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run plain 1 GiB device copies (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -50,56 +63,27 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-class Linear:
-    """One packed linear with its resident x and y."""
+def kernel_sources_sha():
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "mfma.hip", "spectra_internal.h"):
+        with open(os.path.join(ROOT, "dequant_gemv_spectra_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
-    def __init__(self, sp, torch, lin, cfg, M, copy=0):
+
+class Linear:
+    """One packed linear with resident x and y."""
+
+    def __init__(self, sp, torch, lin, cfg, M, W=None, g=None, copy=0):
         from dequant_gemv_spectra_amd import synth
-        W = synth.weights(lin, cfg)
-        g = synth.gamma(lin, cfg)
+        W = synth.weights(lin, cfg) if W is None else W
+        g = synth.gamma(lin, cfg) if g is None else g
         self.c = sp.spectra_pack(W, g)
         self.info = self.c.info()
         self.lin = lin
         self.x = torch.from_numpy(synth.activations(lin, cfg, M, salt=copy)).cuda()
         self.y = torch.empty((M, lin.N), dtype=torch.float16, device="cuda")
-        self.M = M
         self.bytes = (self.info["bytes_payload"] + self.info["bytes_meta"] + 2 * M * lin.K + 2 * M * lin.N)
-
-
-def build_units(args, sp, torch):
-    """Launch units of one step: list of (label, callable, bytes)."""
-    from dequant_gemv_spectra_amd import synth
-    cfg = int(args.workload[3:])
-    wl = synth.workload(cfg, layers=args.layers if cfg == 3 else None)
-    M = args.M
-    kern = args.kernel
-    units = []
-    if cfg in (2, 3):
-        by_layer = {}
-        for lin in wl.linears:
-            by_layer.setdefault(lin.layer, []).append(lin)
-        # the 1.5B-class layer (~28 MB) is stacked 28 deep, the depth of that model
-        depth = 28 if cfg == 2 else 1
-        for layer in sorted(by_layer):
-            for cp in range(depth):
-                t0 = time.time()
-                packed = [Linear(sp, torch, lin, cfg, M, copy=cp) for lin in by_layer[layer]]
-                tag = f"L{layer}" if depth == 1 else f"L{cp}"
-                units.extend(layer_units(sp, packed, M, kern, tag))
-                if layer % 6 == 0 or depth > 1 and cp % 7 == 0:
-                    log(f"{tag}: packed {len(packed)} linears in {time.time() - t0:.1f}s")
-        if cfg == 2:
-            wl.name = "decoder-1.5B-28-layers"
-        return wl, units
-    # single linear: rotate distinct copies past the last-level cache
-    lin = wl.linears[0]
-    first = Linear(sp, torch, lin, cfg, M)
-    copies = max(1, int(args.rotate_gib * 2 ** 30 // first.bytes) + 1)
-    packed = [first] + [Linear(sp, torch, lin, cfg, M, copy=cp) for cp in range(1, copies)]
-    log(f"{wl.name}: {copies} distinct copies, {first.bytes / 1e6:.1f} MB each")
-    for i, p in enumerate(packed):
-        units.append((f"{lin.name}#{i}", gemm_call(sp, p, kern), p.bytes))
-    return wl, units
 
 
 def gemm_call(sp, p, kern):
@@ -108,64 +92,134 @@ def gemm_call(sp, p, kern):
     return f
 
 
+def grouped_call(sp, ps):
+    cs = [p.c for p in ps]
+    ys = [p.y for p in ps]
+    x = ps[0].x
+
+    def f():
+        sp.spectra_gemm_grouped(cs, x, ys)
+    return f
+
+
 def layer_units(sp, packed, M, kern, tag):
+    """Launch units of one decoder layer: (label, kind, callable, bytes)."""
     by = {p.lin.name.split(".")[-1]: p for p in packed}
-    units = []
     if M == 1 and kern in ("auto", "gemv"):
-        qkv = [by["q"], by["k"], by["v"]]
-        gu = [by["gate"], by["up"]]
-
-        def grouped(ps):
-            cs = [p.c for p in ps]
-            ys = [p.y for p in ps]
-            x = ps[0].x
-
-            def f():
-                sp.spectra_gemm_grouped(cs, x, ys)
-            return f
-        units.append((f"{tag}.qkv", grouped(qkv), sum(p.bytes for p in qkv) - 2 * 2 * qkv[0].lin.K))
-        units.append((f"{tag}.o", gemm_call(sp, by["o"], kern), by["o"].bytes))
-        units.append((f"{tag}.gate_up", grouped(gu), sum(p.bytes for p in gu) - 2 * gu[0].lin.K))
-        units.append((f"{tag}.down", gemm_call(sp, by["down"], kern), by["down"].bytes))
-    else:
-        for nm in ("q", "k", "v", "o", "gate", "up", "down"):
-            units.append((f"{tag}.{nm}", gemm_call(sp, by[nm], kern), by[nm].bytes))
-    return units
+        qkv, gu = [by["q"], by["k"], by["v"]], [by["gate"], by["up"]]
+        return [(f"{tag}.qkv", "qkv", grouped_call(sp, qkv), sum(p.bytes for p in qkv) - 2 * 2 * by["q"].lin.K),
+                (f"{tag}.o", "o", gemm_call(sp, by["o"], kern), by["o"].bytes),
+                (f"{tag}.gate_up", "gate_up", grouped_call(sp, gu), sum(p.bytes for p in gu) - 2 * by["gate"].lin.K),
+                (f"{tag}.down", "down", gemm_call(sp, by["down"], kern), by["down"].bytes)]
+    return [(f"{tag}.{nm}", nm, gemm_call(sp, by[nm], kern), by[nm].bytes)
+            for nm in ("q", "k", "v", "o", "gate", "up", "down")]
 
 
-def cpu_baseline(wl, units_meta, budget_s=20.0):
-    """The oracle's product (unpack + float64 x W_hat^T) on a bounded sample."""
-    import numpy as np
+def build_units(args, sp, torch):
+    from dequant_gemv_spectra_amd import synth
+    cfg = int(args.workload[3:])
+    wl = synth.workload(cfg, layers=args.layers if cfg == 3 else None)
+    M, kern = args.M, args.kernel
+    units = []
+    if cfg in (2, 3):
+        by_layer = {}
+        for lin in wl.linears:
+            by_layer.setdefault(lin.layer, []).append(lin)
+        depth = 28 if cfg == 2 else 1  # the 1.5B-class model is 28 layers deep
+        cache = {}
+        for layer in sorted(by_layer):
+            for cp in range(depth):
+                t0 = time.time()
+                packed = []
+                for lin in by_layer[layer]:
+                    if lin.name not in cache:
+                        cache[lin.name] = (synth.weights(lin, cfg), synth.gamma(lin, cfg))
+                    W, g = cache[lin.name]
+                    packed.append(Linear(sp, torch, lin, cfg, M, W, g, copy=cp))
+                units.extend(layer_units(sp, packed, M, kern, f"L{layer if depth == 1 else cp}"))
+                if (layer if depth == 1 else cp) % 6 == 0:
+                    log(f"layer {layer if depth == 1 else cp}: packed in {time.time() - t0:.1f}s")
+            if depth == 1:
+                cache.clear()
+        name = wl.name if cfg == 3 else "decoder-1.5B-28-layers"
+        return name, units, True
+    lin = wl.linears[0]
+    W, g = synth.weights(lin, cfg), synth.gamma(lin, cfg)
+    first = Linear(sp, torch, lin, cfg, M, W, g)
+    copies = max(1, int(args.rotate_gib * 2 ** 30 // first.bytes) + 1)
+    packed = [first] + [Linear(sp, torch, lin, cfg, M, W, g, copy=cp) for cp in range(1, copies)]
+    log(f"{wl.name}: {copies} distinct copies, {first.bytes / 1e6:.1f} MB each")
+    units = [(f"{lin.name}#{i}", lin.name, gemm_call(sp, p, kern), p.bytes) for i, p in enumerate(packed)]
+    return wl.name, units, False
+
+
+_CAPTURE_STREAM = None
+
+
+def capture(torch, fns):
+    """Capture fns into a graph on one fixed side stream; an eager pass on the
+    same stream first lets the library size its per-stream workspace outside
+    capture."""
+    global _CAPTURE_STREAM
+    if _CAPTURE_STREAM is None:
+        _CAPTURE_STREAM = torch.cuda.Stream()
+    s = _CAPTURE_STREAM
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps):
+    s = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    z = torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(reps):
+        g.replay()
+    z.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(z) / reps  # ms
+
+
+def cpu_baseline(metas, min_s=10.0):
+    """The oracle's product (unpack + float64 x W_hat^T) on a bounded sample:
+    the sample's linears in order, repeated until at least min_s of CPU work."""
     from oracle import spectra_oracle as O
     try:
         from threadpoolctl import threadpool_info
         blas = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
     except Exception:
         blas = 1
-    done_bytes = 0
-    t_total = 0.0
-    names = []
-    for name, img, x, nbytes in units_meta:
-        t0 = time.perf_counter()
-        W_hat = O.unpack(img)["W_hat"]
-        O.matmul_ref(W_hat, x)
-        t_total += time.perf_counter() - t0
-        done_bytes += nbytes
-        names.append(name)
-        if t_total > budget_s:
-            break
+    done_bytes, t_total, names, rounds = 0, 0.0, [], 0
+    while t_total < min_s:
+        for name, img, x, nbytes in metas:
+            t0 = time.perf_counter()
+            O.matmul_ref(O.unpack(img)["W_hat"], x)
+            t_total += time.perf_counter() - t0
+            done_bytes += nbytes
+            if rounds == 0:
+                names.append(name)
+        rounds += 1
     return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": int(blas),
             "kind": "oracle",
-            "sample": f"oracle unpack + float64 product of {len(names)} linears "
-                      f"({', '.join(names)}), {done_bytes / 1e6:.1f} MB algorithmic, {t_total:.1f} s; "
-                      f"cores = BLAS threads of the product (unpack is single-threaded numpy)"}
+            "sample": f"oracle unpack + float64 product of {len(names)} linear(s) ({', '.join(names)}) "
+                      f"x {rounds} rounds, {done_bytes / 1e6:.1f} MB algorithmic in {t_total:.1f} s; "
+                      f"cores = BLAS threads of the product (the unpack is single-threaded numpy)"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the dequant-GEMV path "
-                                   "has no multi-GPU mode (--gpus 1)"}))
+        print(json.dumps({"error": "the dequant-GEMV path runs on one GPU; multi-GPU runs are not "
+                                   "part of this benchmark (use --gpus 1)"}))
         sys.exit(2)
     import numpy as np
     import torch
@@ -173,102 +227,93 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
-    sp.lib()
+    sp.lib()  # fails loudly when the HIP library is missing
     torch.cuda.set_device(0)
-    t0 = time.time()
-    wl, units = build_units(args, sp, torch)
-    torch.cuda.synchronize()
-    log(f"setup {time.time() - t0:.1f}s, {len(units)} launches per step")
+    if args.calibrate_copy:  # plain copies of known size, for counter scale factors
+        a = torch.empty(2 ** 29, dtype=torch.float16, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": a.numel() * 2, "written": b.numel() * 2, "copies": 5}))
+        return
     cfg = int(args.workload[3:])
-    bytes_per_step = sum(b for _, _, b in units) if cfg in (2, 3) else None
-
-    def run_step(i):
-        if cfg in (2, 3):
-            for _, f, _ in units:
-                f()
-        else:
-            units[i % len(units)][1]()
-
-    stream = torch.cuda.current_stream()
-    use_graph = (cfg in (2, 3)) and not args.no_graph
-    graph = None
-    if use_graph:
-        run_step(0)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            run_step(0)
-        torch.cuda.synchronize()
-
-    def step(i):
-        if graph is not None:
-            graph.replay()
-        else:
-            run_step(i)
-
-    for i in range(args.warmup):
-        step(i)
+    t0 = time.time()
+    name, units, layered = build_units(args, sp, torch)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record(stream)
+    log(f"setup {time.time() - t0:.1f}s, {len(units)} launches per pass")
+
+    pass_bytes = sum(u[3] for u in units)
+    if args.eager:  # counter runs: plain launches, no graphs, no timing claims
+        for _ in range(max(1, args.steps)):
+            for u in units:
+                u[2]()
+        torch.cuda.synchronize()
+        print(json.dumps({"eager_passes": max(1, args.steps), "launches_per_pass": len(units),
+                          "bytes_per_pass": int(pass_bytes)}))
+        return
+    graph = capture(torch, [u[2] for u in units])
+    for _ in range(args.warmup):
+        graph.replay()
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_per_step = ms_total / args.steps
-    if cfg in (1, 4, 5):
-        bytes_per_step = units[0][2]
+    if layered:  # one step = one pass over every layer
+        ms_per_step = time_graph(torch, graph, args.steps)
+        bytes_per_step = pass_bytes
+        launches = len(units)
+    else:        # one step = one linear; a replay launches every rotated copy once
+        reps = max(1, args.steps // len(units))
+        ms_per_step = time_graph(torch, graph, reps) / len(units)
+        bytes_per_step = pass_bytes / len(units)
+        launches = 1
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
-    # Roofline of the dominant kernel: per-launch HIP events (on the launch
-    # stream) around each launch of the largest launch unit kind, eager.
-    if cfg in (2, 3):
-        kinds = {}
-        for lab, f, b in units:
-            kinds.setdefault(lab.split(".")[-1], []).append((f, b))
-        dom = max(kinds, key=lambda k: sum(b for _, b in kinds[k]))
-        dom_units = kinds[dom]
-    else:
-        dom = wl.linears[0].name
-        dom_units = [(f, b) for _, f, b in units]
-    durs = []
-    nb = []
-    reps = max(1, min(args.steps, 10))
-    evs = []
-    for r in range(reps):
-        for f, b in dom_units:
-            a = torch.cuda.Event(enable_timing=True)
-            z = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            f()
-            z.record(stream)
-            evs.append((a, z, b))
-    torch.cuda.synchronize()
-    for a, z, b in evs:
-        durs.append(a.elapsed_time(z))
-        nb.append(b)
-    avg_ms = float(np.mean(durs))
-    avg_bytes = float(np.mean(nb))
-    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+    # roofline of the dominant kernel kind
+    kinds = {}
+    for _, kind, f, b in units:
+        kinds.setdefault(kind, []).append((f, b))
+    dom = max(kinds, key=lambda k: sum(b for _, b in kinds[k]))
+    dgraph = capture(torch, [f for f, _ in kinds[dom]])
+    dgraph.replay()
+    dms = time_graph(torch, dgraph, 10) / len(kinds[dom])
+    dbytes = sum(b for _, b in kinds[dom]) / len(kinds[dom])
+    achieved = dbytes / (dms * 1e-3) / 1e9
+    kernel_name = "k_gemv_m1" if (args.M == 1 and args.kernel != "mfma") else "k_mfma"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": dom, "avg_launch_us": round(avg_ms * 1e3, 2),
-                "bytes_per_launch": int(avg_bytes), "launches_timed": len(durs)}
+                "kernel": f"{kernel_name} ({dom} launches)", "avg_launch_us": round(dms * 1e3, 3),
+                "bytes_per_launch": int(dbytes), "launches_timed": 10 * len(kinds[dom])}
+    if args.M > 1:  # past the ridge point the contraction is bound by the matrix cores
+        from dequant_gemv_spectra_amd import synth
+        lins = synth.workload(cfg, layers=1 if cfg == 3 else None).linears
+        per = {l.name.split(".")[-1]: 2.0 * args.M * l.N * l.K for l in lins}
+        dflops = per.get(dom, per[lins[0].name.split(".")[-1]])
+        if dflops / dbytes > PEAK_MFMA_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+            tf = dflops / (dms * 1e-3) / 1e12
+            roofline.update({"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_MFMA_F16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_F16_TFLOPS, 4)})
+        roofline["arith_intensity_flop_per_byte"] = round(dflops / dbytes, 1)
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        key = f"{args.workload}:M{args.M}:{dom}"
+        ent = tr.get("entries", {}).get(key)
+        if ent and ent.get("source_sha") == kernel_sources_sha():
+            roofline["traffic"] = int(ent["hbm_bytes_per_launch"])
+    except (OSError, ValueError):
+        pass
 
     cpu = None
     if not args.no_cpu_baseline:
         from dequant_gemv_spectra_amd import synth
-        sample = wl.linears[:7] if cfg in (2, 3) else wl.linears[:1]
-        meta = []
-        for lin in sample:
+        wl = synth.workload(cfg, layers=1 if cfg == 3 else None)
+        metas = []
+        for lin in (wl.linears[:7] if cfg in (2, 3) else wl.linears[:1]):
             c = sp.spectra_pack(synth.weights(lin, cfg), synth.gamma(lin, cfg))
             info = c.info()
             nbytes = info["bytes_payload"] + info["bytes_meta"] + 2 * args.M * (lin.K + lin.N)
-            meta.append((lin.name, sp.spectra_export(c), synth.activations(lin, cfg, args.M), nbytes))
+            metas.append((lin.name, sp.spectra_export(c), synth.activations(lin, cfg, args.M), nbytes))
             c.close()
-        cpu = cpu_baseline(wl, meta)
+        cpu = cpu_baseline(metas)
 
     out = {
         "metric": METRIC,
@@ -283,12 +328,10 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "M": args.M, "linears": len(wl.linears),
-                   "launches_per_step": len(units) if cfg in (2, 3) else 1,
+        "config": {"workload": name, "M": args.M, "launches_per_step": launches,
                    "bytes_per_step": int(bytes_per_step),
                    "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
-                   "graph": graph is not None, "kernel": args.kernel,
-                   "parallelism": "single GPU"},
+                   "hip_graph": True, "kernel": args.kernel, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

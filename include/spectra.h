@@ -9,7 +9,7 @@
  * channels to exact floating-point storage, and the Gaussian bulk to Group-32
  * 4-bit codes with per-group scales and bit-packed zero points; fused GPU
  * kernels then dequantize inside the matrix-vector product at decode batch
- * sizes (same page, highlight 4, "High-Efficiency Fused ... Kernels").
+ * sizes (same page, highlight 4 on its fused kernels).
  * The page fixes neither formulas nor a memory layout.  Every choice below that
  * it leaves open is stated where it is made, as this library's reading.
  *
@@ -25,8 +25,9 @@
  *     (exact in binary64).  mean = sum_n s[n] / N; m2 = sum_n (s[n]-mean)^2 / N;
  *     m4 = sum_n ((s[n]-mean)^2)^2 / N.  Channel k is heavy-tailed iff m2 > 0
  *     and m4/(m2*m2) - 3 > 3.0 (excess kurtosis with population moments; the
- *     page gives only "kurtosis > 3.0" -- this library reads it as excess
- *     kurtosis, under which Gaussian columns are essentially never flagged).
+ *     page names only a fourth-moment test with threshold 3.0 -- this library
+ *     reads it as excess kurtosis, under which Gaussian columns are
+ *     essentially never flagged).
  *     A constant column (N = 1, gamma[k] = 0, ...) has m2 = 0 and is bulk.
  *     The device evaluates the sums in a fixed tree order, so a channel whose
  *     kurtosis lies within a few ulp of the threshold may be classified
