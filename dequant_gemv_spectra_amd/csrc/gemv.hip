@@ -439,6 +439,8 @@ hipError_t launch_tasks(GemvTasks& ts, hipStream_t s) {
 
 bool gemv_supports(const DeviceView& v, int64_t M) {
   if (M != 1) return false;
+  // a block stages at most kXChunks * 8 * kBlock channels and kQuads * 4 * kBlock bulk positions
+  if (v.K > kXChunks * 8 * kBlock || (int64_t)kGroup * v.G > (int64_t)kQuads * 4 * kBlock) return false;
   if (pick_variant(v.G).P == 0) return false;
   return lds_bytes(v) <= kMaxLds;
 }

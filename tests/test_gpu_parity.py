@@ -113,6 +113,33 @@ def test_pack_bitexact_and_product_small(N, K, n_out, seed):
     check_product(c, img, x)
 
 
+GEMV_EDGE = [  # (N, K, planted heavy-tailed channels, seed): the x-staging limits of the GEMV
+    (50, 12288, 120, 16),  # K at the 12288-channel staging limit
+    (20, 12287, 0, 17),    # K % 8 == 7 at the limit (short columns: kurtosis flags some anyway)
+    (37, 7777, 20, 18),    # K % 8 == 1: a partial last x chunk
+    (3, 8191, 64, 19),     # K % 8 == 7, three rows
+    (90, 130, 129, 20),    # more heavy-tailed channels than bulk ones (n_out 84, G 2)
+]
+
+
+@pytest.mark.parametrize("N,K,n_out,seed", GEMV_EDGE)
+def test_gemv_staging_edges(N, K, n_out, seed):
+    W, g, x = synth.random_case(N, K, n_out, seed)
+    c, img = check_pack(W, g)
+    check_product(c, img, x, kernel="gemv")
+
+
+def test_gemv_beyond_staging_limit_falls_back():
+    """K > 12288: the GEMV declines, auto takes the MFMA path."""
+    sp, torch = _sp(), _torch()
+    W, g, x = synth.random_case(24, 12800, 100, 25)
+    c, img = check_pack(W, g)
+    check_product(c, img, x)  # auto
+    with pytest.raises(sp.SpectraError) as ei:
+        sp.spectra_gemm(c, torch.from_numpy(x).cuda(), kernel="gemv")
+    assert ei.value.status == sp.SPECTRA_E_UNSUPPORTED
+
+
 def test_golden_container_on_gpu():
     sp = _sp()
     W = np.zeros((8, 3), dtype=np.float16)
