@@ -204,11 +204,14 @@ __device__ void stage_x(const DeviceView& v, const uint16_t* __restrict__ x, uin
 }
 
 // Registers holding one tile of weights for a lane: U rows x P groups of
-// codes, scale bits | zero byte << 16, and OS heavy-tailed weights per row.
+// codes, scale bits and zero bytes, and OS heavy-tailed weights per row.
+// Scale and zero stay in separate registers until the tile is computed:
+// combining them at load time would make the compiler wait for those loads
+// before it issues the next tile's, which leaves one tile in flight.
 template <int P, int U, int OS>
 struct Frag {
   uint4 c[U][P];
-  uint32_t sz[U][P];
+  uint32_t s[U][P], z[U][P];
   uint32_t o[U][OS];
 };
 
@@ -237,10 +240,9 @@ __device__ __forceinline__ void load_frag(Frag<P, U, OS>& f, const DeviceView& v
       const bool ok = g < G;
       const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? local * 16u : kOob, 0, 0);
       f.c[u][p] = make_uint4(c.x, c.y, c.z, c.w);
-      const uint32_t s = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? local * 2u : kOob, 0, 0);
+      f.s[u][p] = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? local * 2u : kOob, 0, 0);
       const uint32_t zoff = (uint32_t)(((i0 + local) >> 1) - zb0);
-      const uint32_t z = __builtin_amdgcn_raw_buffer_load_b8(rz, ok ? zoff : kOob, 0, 0);
-      f.sz[u][p] = s | (z << 16);
+      f.z[u][p] = __builtin_amdgcn_raw_buffer_load_b8(rz, ok ? zoff : kOob, 0, 0);
     }
 #pragma unroll
     for (int s = 0; s < OS; ++s) {
@@ -277,8 +279,8 @@ __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const Devi
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = (row0 + team + (int64_t)u * T) * G + g;
-      const uint32_t z = (f.sz[u][p] >> (16u + 4u * (uint32_t)(i & 1))) & 0xFu;
-      acc[u] = __builtin_fmaf(h2f((uint16_t)f.sz[u][p]), group_dot(f.c[u][p], z, xr), acc[u]);
+      const uint32_t z = (f.z[u][p] >> (4u * (uint32_t)(i & 1))) & 0xFu;
+      acc[u] = __builtin_fmaf(h2f((uint16_t)f.s[u][p]), group_dot(f.c[u][p], z, xr), acc[u]);
     }
   }
 #pragma unroll
@@ -296,7 +298,7 @@ __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const Devi
   }
 }
 
-template <int L, int P, int U>
+template <int L, int P, int U, bool Pipe>
 __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   constexpr int OS = (L == 16) ? 4 : 2;  // heavy-tailed slots per lane held in registers
   constexpr int T = kBlock / L;          // teams per block
@@ -332,15 +334,35 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   }
   // Two register buffers, unrolled by hand: the next tile is in flight while
   // this one is computed.
-  for (;;) {
-    if (row >= v.N) break;
-    load_frag<L, P, U, OS>(fb, v, row + stride, lt, team);
-    compute_frag<L, P, U, OS>(fa, v, row, lt, team, xs, xor_, xo, task.y);
-    row += stride;
-    if (row >= v.N) break;
-    load_frag<L, P, U, OS>(fa, v, row + stride, lt, team);
-    compute_frag<L, P, U, OS>(fb, v, row, lt, team, xs, xor_, xo, task.y);
-    row += stride;
+  if constexpr (Pipe) {
+    // Blocks with many tiles.  The body has no early exit (a tile
+    // past N loads nothing; its compute is skipped by a branch that holds no
+    // loads) and scheduling barriers keep work on the current tile's values
+    // below the next tile's load instructions: both let the compiler wait for
+    // exactly the current tile, so the next one stays in flight.
+    for (; row < v.N; row += 2 * stride) {
+      load_frag<L, P, U, OS>(fb, v, row + stride, lt, team);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_frag<L, P, U, OS>(fa, v, row, lt, team, xs, xor_, xo, task.y);
+      load_frag<L, P, U, OS>(fa, v, row + 2 * stride, lt, team);
+      __builtin_amdgcn_sched_barrier(0);
+      if (row + stride < v.N) compute_frag<L, P, U, OS>(fb, v, row + stride, lt, team, xs, xor_, xo, task.y);
+    }
+  } else {
+    // Few tiles per block: stop as soon as the block's rows are done, so no
+    // load is issued past them.
+    for (;;) {
+      if (row >= v.N) break;
+      load_frag<L, P, U, OS>(fb, v, row + stride, lt, team);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_frag<L, P, U, OS>(fa, v, row, lt, team, xs, xor_, xo, task.y);
+      row += stride;
+      if (row >= v.N) break;
+      load_frag<L, P, U, OS>(fa, v, row + stride, lt, team);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_frag<L, P, U, OS>(fb, v, row, lt, team, xs, xor_, xo, task.y);
+      row += stride;
+    }
   }
 }
 
@@ -374,6 +396,7 @@ size_t lds_bytes(const DeviceView& v) {
 
 constexpr int kU = SPECTRA_GEMV_U;
 constexpr size_t kMaxLds = 64 * 1024;
+constexpr int64_t kPipeTiles = 6;  // tiles per block from which the loop without early exits pays
 
 // Split the block budget between the tasks in proportion to their rows.
 template <int L>
@@ -398,8 +421,18 @@ int64_t plan_blocks(GemvTasks& ts) {
 
 template <int L, int P>
 hipError_t launch_lp(GemvTasks& ts, size_t lds, hipStream_t s) {
+  constexpr int64_t kTileRows = (int64_t)(kBlock / L) * kU;
   const int64_t blocks = plan_blocks<L>(ts);
-  hipLaunchKernelGGL((k_gemv_m1<L, P, kU>), dim3((unsigned)blocks), dim3(kBlock), lds, s, ts);
+  int64_t most = 0;  // most tiles any block walks
+  for (int i = 0; i < ts.count; ++i) {
+    const int64_t tiles = (ts.t[i].v.N + kTileRows - 1) / kTileRows;
+    const int64_t per = (tiles + ts.t[i].nblocks - 1) / ts.t[i].nblocks;
+    most = per > most ? per : most;
+  }
+  if (most >= kPipeTiles)
+    hipLaunchKernelGGL((k_gemv_m1<L, P, kU, true>), dim3((unsigned)blocks), dim3(kBlock), lds, s, ts);
+  else
+    hipLaunchKernelGGL((k_gemv_m1<L, P, kU, false>), dim3((unsigned)blocks), dim3(kBlock), lds, s, ts);
   return hipGetLastError();
 }
 
