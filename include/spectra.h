@@ -120,7 +120,7 @@ typedef enum {
 typedef enum {
   SPECTRA_KERNEL_AUTO = 0,     /* GEMV for small M where it fits, MFMA otherwise */
   SPECTRA_KERNEL_GEMV = 1,     /* VALU dequant-GEMV (register/LDS x, fp32 accumulate) */
-  SPECTRA_KERNEL_MFMA = 2      /* LDS-dequant tiles feeding v_mfma_f32_16x16x32_f16 */
+  SPECTRA_KERNEL_MFMA = 2      /* register-dequantized (q - z) tiles on v_mfma_f32_16x16x32_f16 */
 } spectra_kernel;
 
 typedef struct {
