@@ -21,8 +21,15 @@
 //
 // Staging.  Each block copies x into LDS and gathers it into bulk order
 // through perm: x and perm are fetched with 16-byte loads in one round trip,
-// after the block has requested its first tile of weights.  In LDS each group's 32 halves occupy an 80-byte slot, which keeps
-// the per-lane 16-byte reads free of bank conflicts.
+// and the block's first tile of weights is requested right behind them, so
+// the gather and its barriers run while that tile is on its way from HBM (a
+// wave's loads complete in issue order: had the tile gone first, the gather
+// would have waited for it).  In LDS each group's 32 halves occupy an 80-byte
+// slot, which keeps the per-lane 16-byte reads free of bank conflicts.  One
+// block of 512 lanes per compute unit keeps the staging to one copy per CU.
+//
+// Code records are read with the non-temporal hint: each is used once, and
+// the hint keeps them from displacing x, perm and the metadata in the caches.
 //
 // Arithmetic.  For a code word w, (w & 0x000F000F) | 0x6400_6400 holds the
 // fp16 values 1024 + q of members (8d, 8d+1); (w & 0x00F000F0) | 0x6400_6400
@@ -37,7 +44,7 @@
 #include "spectra_internal.h"
 
 #ifndef SPECTRA_GEMV_BLOCKS_PER_CU
-#define SPECTRA_GEMV_BLOCKS_PER_CU 2
+#define SPECTRA_GEMV_BLOCKS_PER_CU 1
 #endif
 #ifndef SPECTRA_GEMV_U
 #define SPECTRA_GEMV_U 1
@@ -47,7 +54,7 @@ namespace spectra {
 namespace {
 
 #ifndef SPECTRA_GEMV_BLOCK
-#define SPECTRA_GEMV_BLOCK 256
+#define SPECTRA_GEMV_BLOCK 512
 #endif
 constexpr int kBlock = SPECTRA_GEMV_BLOCK;
 constexpr int kWaves = kBlock / 64;
@@ -100,6 +107,7 @@ __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast
 // branches.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOob = 0x80000000u;  // an offset past every descriptor built here
+constexpr int kStream = 2;  // cache-policy bit nt: streamed data, read once
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_t bytes) {
   const int n = bytes >= 0x7FFFFFFFull ? 0x7FFFFFFF : (int)bytes;
@@ -142,12 +150,15 @@ __device__ __forceinline__ int xs_index(int j) { return (j >> 5) * kXSlot + (j &
 //   B. x is written to LDS as is (`xraw`, channel order); barrier.
 //   C. Each thread reads its 4 positions' values from xraw through the perm
 //      entries and stores them as one 8-byte write into the group slot.
-// Positions past K_b, and channels past K, read zero through the range check
-// of the buffer descriptors.
-constexpr int kQuads = 12;  // perm quads per thread per pass: 12288 positions
-constexpr int kXChunks = 6; // 8-channel x chunks per thread per pass: 12288 channels
-__device__ void stage_x(const DeviceView& v, const uint16_t* __restrict__ x, uint16_t* xs,
-                        uint16_t* xraw, int tid) {
+// `between` runs after the loads of A are issued and before B waits for them:
+// the caller issues its first weight loads there.  Positions past K_b, and
+// channels past K, read zero through the range check of the buffer
+// descriptors.
+constexpr int kQuads = 8;    // perm quads per thread: 8 * 4 * kBlock = 16384 positions
+constexpr int kXChunks = 4;  // 8-channel x chunks per thread: 4 * 8 * kBlock = 16384 channels
+template <class F>
+__device__ __forceinline__ void stage_x(const DeviceView& v, const uint16_t* __restrict__ x,
+                                        uint16_t* xs, uint16_t* xraw, int tid, F&& between) {
   const int K = v.K, K_b = v.K_b, n_out = v.n_out;
   const int xo_base = kXSlot * v.G;  // heavy-tailed x (fp16) follow the group slots
   const int nquad = 8 * v.G;         // 32G / 4
@@ -169,6 +180,7 @@ __device__ void stage_x(const DeviceView& v, const uint16_t* __restrict__ x, uin
     if (kBlock * i >= nquad) break;
     pq[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)(tid + kBlock * i) * 16u, 0, 0);
   }
+  between();
   // B. raw x into LDS (a partial last chunk is read channel by channel)
 #pragma unroll
   for (int i = 0; i < kXChunks; ++i) {
@@ -238,7 +250,7 @@ __device__ __forceinline__ void load_frag(Frag<P, U, OS>& f, const DeviceView& v
       const int g = lt + L * p;
       const uint32_t local = (uint32_t)(row * G + g);
       const bool ok = g < G;
-      const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? local * 16u : kOob, 0, 0);
+      const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? local * 16u : kOob, 0, kStream);
       f.c[u][p] = make_uint4(c.x, c.y, c.z, c.w);
       f.s[u][p] = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? local * 2u : kOob, 0, 0);
       const uint32_t zoff = (uint32_t)(((i0 + local) >> 1) - zb0);
@@ -319,11 +331,14 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   const int64_t stride = (int64_t)task.nblocks * kTileRows;
   int64_t row = (int64_t)(blockIdx.x - task.block_begin) * kTileRows;
 
-  // The first tile's weights are requested before x is staged, so their HBM
-  // latency overlaps the gather and the barrier.
+  // The first tile's weights are requested right behind the x and perm
+  // loads, so their HBM latency overlaps the gather and the barriers.
   Frag<P, U, OS> fa, fb;
-  load_frag<L, P, U, OS>(fa, v, row, lt, team);
-  stage_x(v, task.x, xs, xraw, tid);
+  stage_x(v, task.x, xs, xraw, tid, [&] {
+    __builtin_amdgcn_sched_barrier(0);
+    load_frag<L, P, U, OS>(fa, v, row, lt, team);
+    __builtin_amdgcn_sched_barrier(0);
+  });
   __syncthreads();
 
   float xor_[OS];
