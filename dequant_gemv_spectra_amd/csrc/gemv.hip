@@ -32,13 +32,12 @@
 // the hint keeps them from displacing x, perm and the metadata in the caches.
 //
 // Arithmetic.  For a code word w, (w & 0x000F000F) | 0x6400_6400 holds the
-// fp16 values 1024 + q of members (8d, 8d+1); (w & 0x00F000F0) | 0x6400_6400
-// holds 1024 + 16q of members (8d+2, 8d+3); the same two masks on w >> 8 give
+// fp16 values 1024 + q of members (8d, 8d+1); (w & 0x00F000F0) | 0x5400_5400
+// holds 64 + q of members (8d+2, 8d+3); the same two masks on w >> 8 give
 // members (8d+4, 8d+5) and (8d+6, 8d+7).  Subtracting the fp16 pairs
-// 1024 + z and 1024 + 16z leaves q - z and 16(q - z), both exact.
-// v_dot2_f32_f16 multiplies them by the matching x pairs and accumulates in
-// fp32 (two accumulators; the second is scaled by 1/16 exactly).  The group
-// sum is scaled by s16 in fp32.  The heavy-tailed columns are a dense fp16
+// 1024 + z and 64 + z leaves q - z exactly.  v_dot2_f32_f16 multiplies them
+// by the matching x pairs and accumulates in fp32 (four accumulators).  The
+// group sum is scaled by s16 in fp32.  The heavy-tailed columns are a dense fp16
 // side product in the same pass.  Team partials are reduced with DPP inside
 // 16-lane rows and lane swizzles across rows.
 #include "spectra_internal.h"
@@ -74,6 +73,7 @@ struct GemvTask {
 struct GemvTasks {
   GemvTask t[kMaxTasks];
   int32_t count;
+  uint32_t nib_lo, nib_hi, mag_lo, mag_hi;  // see Nib
 };
 
 template <int CTRL>
@@ -114,30 +114,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
 }
 
-// (a & m) | o in one VALU op (VOP3 on gfx9 takes no literal, so the compiler
-// otherwise splits it into an AND and an OR with literals).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
-  return r;
-}
+// Nibble masks and fp16 magics of a code word.  The masks arrive as kernel
+// arguments (scalar registers) and the magics are moved into vector registers
+// once, so that each (w & mask) | magic compiles to one v_and_or_b32: a gfx9
+// VOP3 encoding takes no literal, and with immediates the compiler emits a
+// separate AND and OR.
+struct Nib {
+  uint32_t lo, hi;    // 0x000F000F and 0x00F000F0
+  uint32_t mlo, mhi;  // 0x64006400 (1024) and 0x54005400 (64)
+};
 
-// sum_e (q_e - z) * x_e over one 16-byte code record, in fp32.
-__device__ __forceinline__ float group_dot(const uint4 c, const uint32_t z, const half2_t* xr) {
-  constexpr uint32_t kLo = 0x000F000Fu, kHi = 0x00F000F0u, kMagic = 0x64006400u;
-  const half2_t zp = as_h2((0x6400u + z) * 0x00010001u);          // 1024 + z
-  const half2_t zp16 = as_h2((0x6400u + 16u * z) * 0x00010001u);  // 1024 + 16 z
+// sum_e (q_e - z) * x_e over one 16-byte code record, in fp32.  Bits 0-3 of
+// each half under exponent 2^10 read as 1024 + q; bits 4-7 under exponent
+// 2^6 read as 64 + q.  Four accumulators keep the dot2 chains short.
+__device__ __forceinline__ float group_dot(const uint4 c, const uint32_t z, const half2_t* xr,
+                                           const Nib nb) {
+  const uint32_t kMagicLo = nb.mlo, kMagicHi = nb.mhi;
+  const half2_t zl = as_h2((0x6400u + z) * 0x00010001u);         // 1024 + z
+  const half2_t zh = as_h2((0x5400u + (z << 4)) * 0x00010001u);  // 64 + z
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float ta = 0.f, tb = 0.f;
+  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t w8 = w[d] >> 8;
-    ta = __builtin_amdgcn_fdot2(as_h2(and_or(w[d], kLo, kMagic)) - zp, xr[4 * d + 0], ta, false);
-    tb = __builtin_amdgcn_fdot2(as_h2(and_or(w[d], kHi, kMagic)) - zp16, xr[4 * d + 1], tb, false);
-    ta = __builtin_amdgcn_fdot2(as_h2(and_or(w8, kLo, kMagic)) - zp, xr[4 * d + 2], ta, false);
-    tb = __builtin_amdgcn_fdot2(as_h2(and_or(w8, kHi, kMagic)) - zp16, xr[4 * d + 3], tb, false);
+    a0 = __builtin_amdgcn_fdot2(as_h2((w[d] & nb.lo) | kMagicLo) - zl, xr[4 * d + 0], a0, false);
+    b0 = __builtin_amdgcn_fdot2(as_h2((w[d] & nb.hi) | kMagicHi) - zh, xr[4 * d + 1], b0, false);
+    a1 = __builtin_amdgcn_fdot2(as_h2((w8 & nb.lo) | kMagicLo) - zl, xr[4 * d + 2], a1, false);
+    b1 = __builtin_amdgcn_fdot2(as_h2((w8 & nb.hi) | kMagicHi) - zh, xr[4 * d + 3], b1, false);
   }
-  return __builtin_fmaf(tb, 0.0625f, ta);
+  return (a0 + a1) + (b0 + b1);
 }
 
 __device__ __forceinline__ int xs_index(int j) { return (j >> 5) * kXSlot + (j & 31); }
@@ -240,6 +245,7 @@ __device__ __forceinline__ void load_frag(Frag<P, U, OS>& f, const DeviceView& v
   const __amdgpu_buffer_rsrc_t rc = rsrc(v.codes + i0, (uint64_t)rows * G * 16);
   const __amdgpu_buffer_rsrc_t rs = rsrc(v.scales + i0, (uint64_t)rows * G * 2);
   const int64_t zb0 = i0 >> 1;
+  const uint32_t i0odd = (uint32_t)(i0 & 1);
   const __amdgpu_buffer_rsrc_t rz = rsrc(v.zeros + zb0, (uint64_t)(((i0 + rows * G + 1) >> 1) - zb0));
   const __amdgpu_buffer_rsrc_t ro = rsrc(v.outliers + row0 * n_out, (uint64_t)rows * n_out * 2);
 #pragma unroll
@@ -253,7 +259,7 @@ __device__ __forceinline__ void load_frag(Frag<P, U, OS>& f, const DeviceView& v
       const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? local * 16u : kOob, 0, kStream);
       f.c[u][p] = make_uint4(c.x, c.y, c.z, c.w);
       f.s[u][p] = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? local * 2u : kOob, 0, 0);
-      const uint32_t zoff = (uint32_t)(((i0 + local) >> 1) - zb0);
+      const uint32_t zoff = (local + i0odd) >> 1;  // byte of group i0 + local, from byte zb0
       f.z[u][p] = __builtin_amdgcn_raw_buffer_load_b8(rz, ok ? zoff : kOob, 0, 0);
     }
 #pragma unroll
@@ -269,7 +275,7 @@ template <int L, int P, int U, int OS>
 __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const DeviceView& v,
                                              int64_t row0, int lt, int team, const uint16_t* xs,
                                              const float* xor_, const uint16_t* xo,
-                                             uint16_t* __restrict__ y) {
+                                             uint16_t* __restrict__ y, const Nib nb) {
   constexpr int T = kBlock / L;
   const int G = v.G, n_out = v.n_out;
   float acc[U];
@@ -290,9 +296,10 @@ __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const Devi
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t i = (row0 + team + (int64_t)u * T) * G + g;
-      const uint32_t z = (f.z[u][p] >> (4u * (uint32_t)(i & 1))) & 0xFu;
-      acc[u] = __builtin_fmaf(h2f((uint16_t)f.s[u][p]), group_dot(f.c[u][p], z, xr), acc[u]);
+      // flat group index (row * G + g): its parity picks the zero nibble
+      const uint32_t odd = (((uint32_t)(row0 + team + (int64_t)u * T) & (uint32_t)G) ^ (uint32_t)g) & 1u;
+      const uint32_t z = (f.z[u][p] >> (4u * odd)) & 0xFu;
+      acc[u] = __builtin_fmaf(h2f((uint16_t)f.s[u][p]), group_dot(f.c[u][p], z, xr, nb), acc[u]);
     }
   }
 #pragma unroll
@@ -320,6 +327,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   for (int i = 1; i < tasks.count; ++i)
     if ((int32_t)blockIdx.x >= tasks.t[i].block_begin) ti = i;
   const GemvTask& task = tasks.t[ti];
+  uint32_t mlo, mhi;  // opaque copies: the compiler cannot fold them back into literals
+  asm volatile("v_mov_b32 %0, %1" : "=v"(mlo) : "s"(tasks.mag_lo));
+  asm volatile("v_mov_b32 %0, %1" : "=v"(mhi) : "s"(tasks.mag_hi));
+  const Nib nb{tasks.nib_lo, tasks.nib_hi, mlo, mhi};
   const DeviceView& v = task.v;
   const int G = v.G, n_out = v.n_out;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
@@ -358,10 +369,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
     for (; row < v.N; row += 2 * stride) {
       load_frag<L, P, U, OS>(fb, v, row + stride, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      compute_frag<L, P, U, OS>(fa, v, row, lt, team, xs, xor_, xo, task.y);
+      compute_frag<L, P, U, OS>(fa, v, row, lt, team, xs, xor_, xo, task.y, nb);
       load_frag<L, P, U, OS>(fa, v, row + 2 * stride, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      if (row + stride < v.N) compute_frag<L, P, U, OS>(fb, v, row + stride, lt, team, xs, xor_, xo, task.y);
+      if (row + stride < v.N) compute_frag<L, P, U, OS>(fb, v, row + stride, lt, team, xs, xor_, xo, task.y, nb);
     }
   } else {
     // Few tiles per block: stop as soon as the block's rows are done, so no
@@ -370,12 +381,12 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
       if (row >= v.N) break;
       load_frag<L, P, U, OS>(fb, v, row + stride, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      compute_frag<L, P, U, OS>(fa, v, row, lt, team, xs, xor_, xo, task.y);
+      compute_frag<L, P, U, OS>(fa, v, row, lt, team, xs, xor_, xo, task.y, nb);
       row += stride;
       if (row >= v.N) break;
       load_frag<L, P, U, OS>(fa, v, row + stride, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      compute_frag<L, P, U, OS>(fb, v, row, lt, team, xs, xor_, xo, task.y);
+      compute_frag<L, P, U, OS>(fb, v, row, lt, team, xs, xor_, xo, task.y, nb);
       row += stride;
     }
   }
@@ -467,6 +478,10 @@ hipError_t launch_l(int P, GemvTasks& ts, size_t lds, hipStream_t s) {
 }
 
 hipError_t launch_tasks(GemvTasks& ts, hipStream_t s) {
+  ts.nib_lo = 0x000F000Fu;
+  ts.nib_hi = 0x00F000F0u;
+  ts.mag_lo = 0x64006400u;
+  ts.mag_hi = 0x54005400u;
   int gmax = 0;
   size_t lds = 0;
   for (int i = 0; i < ts.count; ++i) {
