@@ -45,6 +45,9 @@
 #ifndef SPECTRA_GEMV_BLOCKS_PER_CU
 #define SPECTRA_GEMV_BLOCKS_PER_CU 1
 #endif
+#ifndef SPECTRA_GEMV_TWO_BLOCK_TILES
+#define SPECTRA_GEMV_TWO_BLOCK_TILES 6
+#endif
 #ifndef SPECTRA_GEMV_U
 #define SPECTRA_GEMV_U 1
 #endif
@@ -430,7 +433,14 @@ int64_t plan_blocks(GemvTasks& ts) {
   constexpr int64_t kTileRows = (int64_t)(kBlock / L) * kU;
   int64_t total_rows = 0;
   for (int i = 0; i < ts.count; ++i) total_rows += ts.t[i].v.N;
-  const int64_t budget = (int64_t)ts.t[0].v.cu_count * SPECTRA_GEMV_BLOCKS_PER_CU;
+  // Launches long enough to give every block several tiles run two blocks
+  // per CU (16 waves, so one wave's dequant work overlaps another's loads);
+  // short ones keep one block, whose x staging is then paid once per CU.
+  int64_t all_tiles = 0;
+  for (int i = 0; i < ts.count; ++i) all_tiles += (ts.t[i].v.N + kTileRows - 1) / kTileRows;
+  const int64_t cus = ts.t[0].v.cu_count;
+  const int64_t bpc = all_tiles >= cus * 2 * SPECTRA_GEMV_TWO_BLOCK_TILES ? 2 : SPECTRA_GEMV_BLOCKS_PER_CU;
+  const int64_t budget = cus * bpc;
   int64_t begin = 0;
   for (int i = 0; i < ts.count; ++i) {
     GemvTask& t = ts.t[i];
