@@ -71,6 +71,7 @@ struct GemvTask {
   uint16_t* y;
   int32_t block_begin;  // first block of this task in the grid
   int32_t nblocks;      // blocks serving this task
+  int32_t rows_per_block;  // contiguous rows per block (short launches), else 0
 };
 
 struct GemvTasks {
@@ -235,14 +236,14 @@ struct Frag {
   uint32_t o[U][OS];
 };
 
-// Loads the tile whose first row is row0 (rows >= N read as zero).  The
+// Loads the tile whose first row is row0 (rows >= row_end read as zero).  The
 // descriptors are rebased on the tile so offsets stay small for any size.
 template <int L, int P, int U, int OS>
 __device__ __forceinline__ void load_frag(Frag<P, U, OS>& f, const DeviceView& v, int64_t row0,
-                                          int lt, int team) {
+                                          int64_t row_end, int lt, int team) {
   constexpr int T = kBlock / L;
   const int G = v.G, n_out = v.n_out;
-  const int64_t left = v.N - row0;
+  const int64_t left = row_end - row0;
   const int64_t rows = left < (int64_t)T * U ? (left > 0 ? left : 0) : (int64_t)T * U;
   const int64_t i0 = row0 * G;  // flat group index of the tile's first group
   const __amdgpu_buffer_rsrc_t rc = rsrc(v.codes + i0, (uint64_t)rows * G * 16);
@@ -276,7 +277,8 @@ __device__ __forceinline__ void load_frag(Frag<P, U, OS>& f, const DeviceView& v
 
 template <int L, int P, int U, int OS>
 __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const DeviceView& v,
-                                             int64_t row0, int lt, int team, const uint16_t* xs,
+                                             int64_t row0, int64_t row_end, int lt, int team,
+                                             const uint16_t* xs,
                                              const float* xor_, const uint16_t* xo,
                                              uint16_t* __restrict__ y, const Nib nb) {
   constexpr int T = kBlock / L;
@@ -311,16 +313,20 @@ __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const Devi
     float a = acc[u];
 #pragma unroll
     for (int s = 0; s < OS; ++s) a = __builtin_fmaf(xor_[s], h2f((uint16_t)f.o[u][s]), a);
-    if (n < v.N && n_out > L * OS) {  // heavy-tailed columns beyond the register slots
+    if (n < row_end && n_out > L * OS) {  // heavy-tailed columns beyond the register slots
       const uint16_t* orow = v.outliers + n * n_out;
       for (int j = lt + L * OS; j < n_out; j += L) a = __builtin_fmaf(h2f(xo[j]), h2f(orow[j]), a);
     }
     const float s = team_sum<L>(a);
-    if (lt == 0 && n < v.N) y[n] = f2h(s);
+    if (lt == 0 && n < row_end) y[n] = f2h(s);
   }
 }
 
-template <int L, int P, int U, bool Pipe>
+// NT == 0: the block walks the tiles b, b + B, b + 2B, ... of its container
+// (long launches).  NT >= 1: the block owns rows_per_block consecutive rows,
+// at most NT tiles (short launches: every block gets the same number of rows,
+// where whole tiles would leave some blocks a tile more than others).
+template <int L, int P, int U, int NT>
 __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   constexpr int OS = (L == 16) ? 4 : 2;  // heavy-tailed slots per lane held in registers
   constexpr int T = kBlock / L;          // teams per block
@@ -342,15 +348,18 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   const int tid = threadIdx.x;
   const int lt = tid % L;
   const int team = tid / L;
-  const int64_t stride = (int64_t)task.nblocks * kTileRows;
-  int64_t row = (int64_t)(blockIdx.x - task.block_begin) * kTileRows;
+  const int64_t lb = (int64_t)(blockIdx.x - task.block_begin);
+  // NT >= 1: rows [row, end) in tiles of kTileRows; NT == 0: tiles `stride` apart
+  const int64_t stride = NT ? (int64_t)kTileRows : (int64_t)task.nblocks * kTileRows;
+  int64_t row = NT ? lb * task.rows_per_block : lb * kTileRows;
+  const int64_t end = NT ? (row + task.rows_per_block < v.N ? row + task.rows_per_block : v.N) : v.N;
 
   // The first tile's weights are requested right behind the x and perm
   // loads, so their HBM latency overlaps the gather and the barriers.
   Frag<P, U, OS> fa, fb;
   stage_x(v, task.x, xs, xraw, tid, [&] {
     __builtin_amdgcn_sched_barrier(0);
-    load_frag<L, P, U, OS>(fa, v, row, lt, team);
+    load_frag<L, P, U, OS>(fa, v, row, end, lt, team);
     __builtin_amdgcn_sched_barrier(0);
   });
   __syncthreads();
@@ -361,36 +370,31 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
     const int j = lt + L * s;
     xor_[s] = j < n_out ? h2f(xo[j]) : 0.f;
   }
-  // Two register buffers, unrolled by hand: the next tile is in flight while
-  // this one is computed.
-  if constexpr (Pipe) {
-    // Blocks with many tiles.  The body has no early exit (a tile
-    // past N loads nothing; its compute is skipped by a branch that holds no
-    // loads) and scheduling barriers keep work on the current tile's values
-    // below the next tile's load instructions: both let the compiler wait for
-    // exactly the current tile, so the next one stays in flight.
-    for (; row < v.N; row += 2 * stride) {
-      load_frag<L, P, U, OS>(fb, v, row + stride, lt, team);
+  // Two register buffers: the next tile is in flight while this one is
+  // computed.  Neither form has an early exit between a load and the compute
+  // that uses it (a tile past `end` loads nothing and its compute is skipped
+  // by a branch that holds no loads), and scheduling barriers keep work on
+  // the current tile's values below the next tile's load instructions: both
+  // let the compiler wait for exactly the current tile, so the next one
+  // stays in flight.
+  if constexpr (NT >= 1) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      Frag<P, U, OS>& cur = (t & 1) ? fb : fa;
+      Frag<P, U, OS>& nxt = (t & 1) ? fa : fb;
+      if (t + 1 < NT) load_frag<L, P, U, OS>(nxt, v, row + (t + 1) * stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      compute_frag<L, P, U, OS>(fa, v, row, lt, team, xs, xor_, xo, task.y, nb);
-      load_frag<L, P, U, OS>(fa, v, row + 2 * stride, lt, team);
-      __builtin_amdgcn_sched_barrier(0);
-      if (row + stride < v.N) compute_frag<L, P, U, OS>(fb, v, row + stride, lt, team, xs, xor_, xo, task.y, nb);
+      if (row + t * stride < end)
+        compute_frag<L, P, U, OS>(cur, v, row + t * stride, end, lt, team, xs, xor_, xo, task.y, nb);
     }
   } else {
-    // Few tiles per block: stop as soon as the block's rows are done, so no
-    // load is issued past them.
-    for (;;) {
-      if (row >= v.N) break;
-      load_frag<L, P, U, OS>(fb, v, row + stride, lt, team);
+    for (; row < v.N; row += 2 * stride) {
+      load_frag<L, P, U, OS>(fb, v, row + stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      compute_frag<L, P, U, OS>(fa, v, row, lt, team, xs, xor_, xo, task.y, nb);
-      row += stride;
-      if (row >= v.N) break;
-      load_frag<L, P, U, OS>(fa, v, row + stride, lt, team);
+      compute_frag<L, P, U, OS>(fa, v, row, end, lt, team, xs, xor_, xo, task.y, nb);
+      load_frag<L, P, U, OS>(fa, v, row + 2 * stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      compute_frag<L, P, U, OS>(fb, v, row, lt, team, xs, xor_, xo, task.y, nb);
-      row += stride;
+      if (row + stride < v.N) compute_frag<L, P, U, OS>(fb, v, row + stride, end, lt, team, xs, xor_, xo, task.y, nb);
     }
   }
 }
@@ -428,7 +432,7 @@ constexpr size_t kMaxLds = 64 * 1024;
 constexpr int64_t kPipeTiles = 6;  // tiles per block from which the loop without early exits pays
 
 // Split the block budget between the tasks in proportion to their rows.
-template <int L>
+template <int L, int P>
 int64_t plan_blocks(GemvTasks& ts) {
   constexpr int64_t kTileRows = (int64_t)(kBlock / L) * kU;
   int64_t total_rows = 0;
@@ -436,10 +440,12 @@ int64_t plan_blocks(GemvTasks& ts) {
   // Launches long enough to give every block several tiles run two blocks
   // per CU (16 waves, so one wave's dequant work overlaps another's loads);
   // short ones keep one block, whose x staging is then paid once per CU.
+  // Two blocks fit only while a lane needs at most 128 registers, which
+  // holds up to four slots per lane.
   int64_t all_tiles = 0;
   for (int i = 0; i < ts.count; ++i) all_tiles += (ts.t[i].v.N + kTileRows - 1) / kTileRows;
   const int64_t cus = ts.t[0].v.cu_count;
-  const int64_t bpc = all_tiles >= cus * 2 * SPECTRA_GEMV_TWO_BLOCK_TILES ? 2 : SPECTRA_GEMV_BLOCKS_PER_CU;
+  const int64_t bpc = (P <= 4 && all_tiles >= cus * 2 * SPECTRA_GEMV_TWO_BLOCK_TILES) ? 2 : SPECTRA_GEMV_BLOCKS_PER_CU;
   const int64_t budget = cus * bpc;
   int64_t begin = 0;
   for (int i = 0; i < ts.count; ++i) {
@@ -458,17 +464,34 @@ int64_t plan_blocks(GemvTasks& ts) {
 template <int L, int P>
 hipError_t launch_lp(GemvTasks& ts, size_t lds, hipStream_t s) {
   constexpr int64_t kTileRows = (int64_t)(kBlock / L) * kU;
-  const int64_t blocks = plan_blocks<L>(ts);
-  int64_t most = 0;  // most tiles any block walks
+  const int64_t blocks = plan_blocks<L, P>(ts);
+  int64_t most = 0;  // most tiles any block walks when blocks take whole tiles in turn
   for (int i = 0; i < ts.count; ++i) {
     const int64_t tiles = (ts.t[i].v.N + kTileRows - 1) / kTileRows;
     const int64_t per = (tiles + ts.t[i].nblocks - 1) / ts.t[i].nblocks;
     most = per > most ? per : most;
   }
-  if (most >= kPipeTiles)
-    hipLaunchKernelGGL((k_gemv_m1<L, P, kU, true>), dim3((unsigned)blocks), dim3(kBlock), lds, s, ts);
-  else
-    hipLaunchKernelGGL((k_gemv_m1<L, P, kU, false>), dim3((unsigned)blocks), dim3(kBlock), lds, s, ts);
+  const dim3 grid((unsigned)blocks), block(kBlock);
+  if (most >= kPipeTiles) {
+    for (int i = 0; i < ts.count; ++i) ts.t[i].rows_per_block = 0;
+    hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 0>), grid, block, lds, s, ts);
+    return hipGetLastError();
+  }
+  // Short launch: equal row ranges per block, at most nt tiles each.
+  int64_t nt = 1;
+  for (int i = 0; i < ts.count; ++i) {
+    const int64_t r = (ts.t[i].v.N + ts.t[i].nblocks - 1) / ts.t[i].nblocks;
+    ts.t[i].rows_per_block = (int32_t)r;
+    const int64_t t = (r + kTileRows - 1) / kTileRows;
+    nt = t > nt ? t : nt;
+  }
+  switch (nt) {
+    case 1: hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 1>), grid, block, lds, s, ts); break;
+    case 2: hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 2>), grid, block, lds, s, ts); break;
+    case 3: hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 3>), grid, block, lds, s, ts); break;
+    case 4: hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 4>), grid, block, lds, s, ts); break;
+    default: hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 5>), grid, block, lds, s, ts); break;
+  }
   return hipGetLastError();
 }
 
