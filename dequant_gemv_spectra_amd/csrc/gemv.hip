@@ -78,6 +78,7 @@ struct GemvTasks {
   GemvTask t[kMaxTasks];
   int32_t count;
   uint32_t nib_lo, nib_hi, mag_lo, mag_hi;  // see Nib
+  int32_t m_rows;                           // rows of x (and y) of the launch, <= MX
 };
 
 template <int CTRL>
@@ -128,23 +129,67 @@ struct Nib {
   uint32_t mlo, mhi;  // 0x64006400 (1024) and 0x54005400 (64)
 };
 
-// sum_e (q_e - z) * x_e over one 16-byte code record, in fp32.  Bits 0-3 of
-// each half under exponent 2^10 read as 1024 + q; bits 4-7 under exponent
-// 2^6 read as 64 + q.  Four accumulators keep the dot2 chains short.
-__device__ __forceinline__ float group_dot(const uint4 c, const uint32_t z, const half2_t* xr,
-                                           const Nib nb) {
-  const uint32_t kMagicLo = nb.mlo, kMagicHi = nb.mhi;
+// The 32 members of one 16-byte code record as exact fp16 pairs q - z.  Bits
+// 0-3 of each half under exponent 2^10 read as 1024 + q; bits 4-7 under
+// exponent 2^6 read as 64 + q.  Pair j holds members (2j, 2j + 1), the order
+// of x in the group slot.
+__device__ __forceinline__ void dequant_record(const uint4 c, const uint32_t z, const Nib nb,
+                                               half2_t* wq) {
   const half2_t zl = as_h2((0x6400u + z) * 0x00010001u);         // 1024 + z
   const half2_t zh = as_h2((0x5400u + (z << 4)) * 0x00010001u);  // 64 + z
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t w8 = w[d] >> 8;
+    wq[4 * d + 0] = as_h2((w[d] & nb.lo) | nb.mlo) - zl;
+    wq[4 * d + 1] = as_h2((w[d] & nb.hi) | nb.mhi) - zh;
+    wq[4 * d + 2] = as_h2((w8 & nb.lo) | nb.mlo) - zl;
+    wq[4 * d + 3] = as_h2((w8 & nb.hi) | nb.mhi) - zh;
+  }
+}
+
+// The 32 halves of one x group slot, as 16 pairs.
+__device__ __forceinline__ void read_x(const uint16_t* src16, half2_t* xr) {
+  const uint4* src = reinterpret_cast<const uint4*>(src16);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 t = src[q];
+    xr[4 * q + 0] = as_h2(t.x);
+    xr[4 * q + 1] = as_h2(t.y);
+    xr[4 * q + 2] = as_h2(t.z);
+    xr[4 * q + 3] = as_h2(t.w);
+  }
+}
+
+// sum over the 16 pairs of wq * xr in fp32; four accumulators keep the dot2
+// chains short.
+__device__ __forceinline__ float dot_record(const half2_t* wq, const half2_t* xr) {
+  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    a0 = __builtin_amdgcn_fdot2(wq[4 * d + 0], xr[4 * d + 0], a0, false);
+    b0 = __builtin_amdgcn_fdot2(wq[4 * d + 1], xr[4 * d + 1], b0, false);
+    a1 = __builtin_amdgcn_fdot2(wq[4 * d + 2], xr[4 * d + 2], a1, false);
+    b1 = __builtin_amdgcn_fdot2(wq[4 * d + 3], xr[4 * d + 3], b1, false);
+  }
+  return (a0 + a1) + (b0 + b1);
+}
+
+// sum_e (q_e - z) * x_e over one record with the dequantization fused into the
+// dot products (one row of x: the compiler then keeps one group's pairs live).
+__device__ __forceinline__ float group_dot(const uint4 c, const uint32_t z, const half2_t* xr,
+                                           const Nib nb) {
+  const half2_t zl = as_h2((0x6400u + z) * 0x00010001u);
+  const half2_t zh = as_h2((0x5400u + (z << 4)) * 0x00010001u);
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
   float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t w8 = w[d] >> 8;
-    a0 = __builtin_amdgcn_fdot2(as_h2((w[d] & nb.lo) | kMagicLo) - zl, xr[4 * d + 0], a0, false);
-    b0 = __builtin_amdgcn_fdot2(as_h2((w[d] & nb.hi) | kMagicHi) - zh, xr[4 * d + 1], b0, false);
-    a1 = __builtin_amdgcn_fdot2(as_h2((w8 & nb.lo) | kMagicLo) - zl, xr[4 * d + 2], a1, false);
-    b1 = __builtin_amdgcn_fdot2(as_h2((w8 & nb.hi) | kMagicHi) - zh, xr[4 * d + 3], b1, false);
+    a0 = __builtin_amdgcn_fdot2(as_h2((w[d] & nb.lo) | nb.mlo) - zl, xr[4 * d + 0], a0, false);
+    b0 = __builtin_amdgcn_fdot2(as_h2((w[d] & nb.hi) | nb.mhi) - zh, xr[4 * d + 1], b0, false);
+    a1 = __builtin_amdgcn_fdot2(as_h2((w8 & nb.lo) | nb.mlo) - zl, xr[4 * d + 2], a1, false);
+    b1 = __builtin_amdgcn_fdot2(as_h2((w8 & nb.hi) | nb.mhi) - zh, xr[4 * d + 3], b1, false);
   }
   return (a0 + a1) + (b0 + b1);
 }
@@ -159,29 +204,36 @@ __device__ __forceinline__ int xs_index(int j) { return (j >> 5) * kXSlot + (j &
 //   B. x is written to LDS as is (`xraw`, channel order); barrier.
 //   C. Each thread reads its 4 positions' values from xraw through the perm
 //      entries and stores them as one 8-byte write into the group slot.
-// `between` runs after the loads of A are issued and before B waits for them:
-// the caller issues its first weight loads there.  Positions past K_b, and
+// For a batch tile of MX rows of x, B and C run once per row (row m's slots
+// at xs + m * xstride), reusing xraw.  `between` runs after the loads of A
+// are issued and before B waits for them: the caller issues its first weight
+// loads there.  Positions past K_b, and
 // channels past K, read zero through the range check of the buffer
 // descriptors.
 constexpr int kQuads = 8;    // perm quads per thread: 8 * 4 * kBlock = 16384 positions
 constexpr int kXChunks = 4;  // 8-channel x chunks per thread: 4 * 8 * kBlock = 16384 channels
-template <class F>
-__device__ __forceinline__ void stage_x(const DeviceView& v, const uint16_t* __restrict__ x,
-                                        uint16_t* xs, uint16_t* xraw, int tid, F&& between) {
+template <int MX, class F>
+__device__ __forceinline__ void stage_x(const DeviceView& v, const uint16_t* __restrict__ x, int M,
+                                        uint16_t* xs, int xstride, uint16_t* xraw, int tid,
+                                        F&& between) {
   const int K = v.K, K_b = v.K_b, n_out = v.n_out;
   const int xo_base = kXSlot * v.G;  // heavy-tailed x (fp16) follow the group slots
   const int nquad = 8 * v.G;         // 32G / 4
   const int nchunk = (K + 7) >> 3;
   const __amdgpu_buffer_rsrc_t rp = rsrc(v.perm, (uint64_t)K * 4);
-  const __amdgpu_buffer_rsrc_t rx = rsrc(x, (uint64_t)(K >> 3) * 16);  // whole chunks only
-  // A. loads
+  // A. loads (rows m >= M of a batch tile read zeros)
   const uint32_t oidx = __builtin_amdgcn_raw_buffer_load_b32(
       rp, tid < n_out ? (uint32_t)(K_b + tid) * 4u : kOob, 0, 0);
-  u32x4 xv[kXChunks];
+  u32x4 xv[MX][kXChunks];
 #pragma unroll
-  for (int i = 0; i < kXChunks; ++i) {
-    if (kBlock * i >= nchunk) break;  // block-uniform bound
-    xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(tid + kBlock * i) * 16u, 0, 0);
+  for (int m = 0; m < MX; ++m) {
+    // whole chunks only; row m starts 16-byte aligned (K % 8 == 0 whenever MX > 1)
+    const __amdgpu_buffer_rsrc_t rx = rsrc(x + (int64_t)m * K, m < M ? (uint64_t)(K >> 3) * 16 : 0);
+#pragma unroll
+    for (int i = 0; i < kXChunks; ++i) {
+      if (kBlock * i >= nchunk) break;  // block-uniform bound
+      xv[m][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(tid + kBlock * i) * 16u, 0, 0);
+    }
   }
   u32x4 pq[kQuads];
 #pragma unroll
@@ -190,38 +242,43 @@ __device__ __forceinline__ void stage_x(const DeviceView& v, const uint16_t* __r
     pq[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)(tid + kBlock * i) * 16u, 0, 0);
   }
   between();
-  // B. raw x into LDS (a partial last chunk is read channel by channel)
 #pragma unroll
-  for (int i = 0; i < kXChunks; ++i) {
-    if (kBlock * i >= nchunk) break;
-    const int c = tid + kBlock * i;
-    if (c < nchunk) {
-      u32x4 t = xv[i];
-      if (8 * c + 8 > K) {
-        uint32_t h[8];
+  for (int m = 0; m < MX; ++m) {
+    if (m) __syncthreads();  // every thread is done gathering row m - 1 from xraw
+    // B. raw x into LDS (a partial last chunk is read channel by channel)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = 8 * c + e < K ? x[8 * c + e] : 0u;
-        t = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    for (int i = 0; i < kXChunks; ++i) {
+      if (kBlock * i >= nchunk) break;
+      const int c = tid + kBlock * i;
+      if (c < nchunk) {
+        u32x4 t = xv[m][i];
+        if (8 * c + 8 > K) {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = (m < M && 8 * c + e < K) ? x[(int64_t)m * K + 8 * c + e] : 0u;
+          t = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        }
+        *reinterpret_cast<u32x4*>(xraw + 8 * c) = t;
       }
-      *reinterpret_cast<u32x4*>(xraw + 8 * c) = t;
     }
-  }
-  __syncthreads();
-  // C. gather from xraw into the group slots
+    __syncthreads();
+    // C. gather from xraw into row m's group slots
+    uint16_t* xm = xs + m * xstride;
 #pragma unroll
-  for (int i = 0; i < kQuads; ++i) {
-    if (kBlock * i >= nquad) break;
-    const int c = tid + kBlock * i;
-    const int j = 4 * c;
-    const uint32_t a0 = j + 0 < K_b ? xraw[pq[i].x] : 0u;
-    const uint32_t a1 = j + 1 < K_b ? xraw[pq[i].y] : 0u;
-    const uint32_t a2 = j + 2 < K_b ? xraw[pq[i].z] : 0u;
-    const uint32_t a3 = j + 3 < K_b ? xraw[pq[i].w] : 0u;
-    if (c < nquad)
-      *reinterpret_cast<uint2*>(xs + xs_index(j)) = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+    for (int i = 0; i < kQuads; ++i) {
+      if (kBlock * i >= nquad) break;
+      const int c = tid + kBlock * i;
+      const int j = 4 * c;
+      const uint32_t a0 = j + 0 < K_b ? xraw[pq[i].x] : 0u;
+      const uint32_t a1 = j + 1 < K_b ? xraw[pq[i].y] : 0u;
+      const uint32_t a2 = j + 2 < K_b ? xraw[pq[i].z] : 0u;
+      const uint32_t a3 = j + 3 < K_b ? xraw[pq[i].w] : 0u;
+      if (c < nquad)
+        *reinterpret_cast<uint2*>(xm + xs_index(j)) = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+    }
+    if (tid < n_out) xm[xo_base + tid] = xraw[oidx];
+    for (int j = tid + kBlock; j < n_out; j += kBlock) xm[xo_base + j] = xraw[v.perm[K_b + j]];
   }
-  if (tid < n_out) xs[xo_base + tid] = xraw[oidx];
-  for (int j = tid + kBlock; j < n_out; j += kBlock) xs[xo_base + j] = xraw[v.perm[K_b + j]];
 }
 
 // Registers holding one tile of weights for a lane: U rows x P groups of
@@ -275,50 +332,74 @@ __device__ __forceinline__ void load_frag(Frag<P, U, OS>& f, const DeviceView& v
   }
 }
 
-template <int L, int P, int U, int OS>
+// y rows m < M of the tile: MX rows of x share each dequantized record.
+template <int L, int P, int U, int OS, int MX>
 __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const DeviceView& v,
                                              int64_t row0, int64_t row_end, int lt, int team,
-                                             const uint16_t* xs,
-                                             const float* xor_, const uint16_t* xo,
+                                             const uint16_t* xs, int xstride,
+                                             const float (&xor_)[MX][OS], int M,
                                              uint16_t* __restrict__ y, const Nib nb) {
   constexpr int T = kBlock / L;
   const int G = v.G, n_out = v.n_out;
-  float acc[U];
+  // The x slots are the same for every tile.  With several rows of x the
+  // compiler would keep all of them in registers across tiles (MX * P * 16,
+  // which spills); an opaque zero in the address makes it read them per tile.
+  int x0 = 0, slot_dep = 0;
+  if constexpr (MX > 1) asm volatile("v_mov_b32 %0, 0" : "=v"(x0));
+  float acc[MX][U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) acc[u] = 0.f;
+  for (int m = 0; m < MX; ++m)
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[m][u] = 0.f;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int g = lt + L * p;
-    half2_t xr[16];
-    const uint4* src = reinterpret_cast<const uint4*>(xs + (g < G ? g : 0) * kXSlot);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 t = src[q];
-      xr[4 * q + 0] = as_h2(t.x);
-      xr[4 * q + 1] = as_h2(t.y);
-      xr[4 * q + 2] = as_h2(t.z);
-      xr[4 * q + 3] = as_h2(t.w);
-    }
+    const int slot = (g < G ? g : 0) * kXSlot + x0 + slot_dep;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // flat group index (row * G + g): its parity picks the zero nibble
       const uint32_t odd = (((uint32_t)(row0 + team + (int64_t)u * T) & (uint32_t)G) ^ (uint32_t)g) & 1u;
       const uint32_t z = (f.z[u][p] >> (4u * odd)) & 0xFu;
-      acc[u] = __builtin_fmaf(h2f((uint16_t)f.s[u][p]), group_dot(f.c[u][p], z, xr, nb), acc[u]);
+      const float sc = h2f((uint16_t)f.s[u][p]);
+      if constexpr (MX == 1) {
+        half2_t xr[16];
+        read_x(xs + slot, xr);
+        acc[0][u] = __builtin_fmaf(sc, group_dot(f.c[u][p], z, xr, nb), acc[0][u]);
+      } else {
+        half2_t wq[16];
+        dequant_record(f.c[u][p], z ^ slot_dep, nb, wq);
+        int mdep = 0;  // four rows: the x reads of row m + 2 wait for row m's products
+#pragma unroll
+        for (int m = 0; m < MX; ++m) {
+          half2_t xr[16];
+          read_x(xs + m * xstride + slot + mdep, xr);
+          acc[m][u] = __builtin_fmaf(sc, dot_record(wq, xr), acc[m][u]);
+          if (MX > 2 && m % 2 == 1) asm volatile("" : "+v"(mdep) : "v"(acc[m][u]));
+        }
+        // The next group's x reads and dequantization take an opaque zero
+        // produced after this group's products: one group in registers at a
+        // time (16 pairs + MX * 16 x values), else the compiler front-loads
+        // every group and spills.
+        asm volatile("" : "+v"(slot_dep) : "v"(acc[MX - 1][u]));
+      }
     }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t n = row0 + team + (int64_t)u * T;
-    float a = acc[u];
 #pragma unroll
-    for (int s = 0; s < OS; ++s) a = __builtin_fmaf(xor_[s], h2f((uint16_t)f.o[u][s]), a);
-    if (n < row_end && n_out > L * OS) {  // heavy-tailed columns beyond the register slots
-      const uint16_t* orow = v.outliers + n * n_out;
-      for (int j = lt + L * OS; j < n_out; j += L) a = __builtin_fmaf(h2f(xo[j]), h2f(orow[j]), a);
+    for (int m = 0; m < MX; ++m) {
+      float a = acc[m][u];
+#pragma unroll
+      for (int s = 0; s < OS; ++s) a = __builtin_fmaf(xor_[m][s], h2f((uint16_t)f.o[u][s]), a);
+      if (n < row_end && n_out > L * OS) {  // heavy-tailed columns beyond the register slots
+        const uint16_t* orow = v.outliers + n * n_out;
+        const uint16_t* xo = xs + m * xstride + kXSlot * G;
+        for (int j = lt + L * OS; j < n_out; j += L) a = __builtin_fmaf(h2f(xo[j]), h2f(orow[j]), a);
+      }
+      const float s = team_sum<L>(a);
+      if (lt == 0 && n < row_end && m < M) y[(int64_t)m * v.N + n] = f2h(s);
     }
-    const float s = team_sum<L>(a);
-    if (lt == 0 && n < row_end) y[n] = f2h(s);
   }
 }
 
@@ -326,7 +407,9 @@ __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const Devi
 // (long launches).  NT >= 1: the block owns rows_per_block consecutive rows,
 // at most NT tiles (short launches: every block gets the same number of rows,
 // where whole tiles would leave some blocks a tile more than others).
-template <int L, int P, int U, int NT>
+//
+// MX rows of x (a batch tile, M <= MX) share every dequantized record.
+template <int L, int P, int U, int NT, int MX>
 __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   constexpr int OS = (L == 16) ? 4 : 2;  // heavy-tailed slots per lane held in registers
   constexpr int T = kBlock / L;          // teams per block
@@ -342,9 +425,9 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   const Nib nb{tasks.nib_lo, tasks.nib_hi, mlo, mhi};
   const DeviceView& v = task.v;
   const int G = v.G, n_out = v.n_out;
+  const int xstride = ((kXSlot * G + n_out) + 7) & ~7;  // halves per x row; 16-byte multiple
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  const uint16_t* xo = xs + kXSlot * G;
-  uint16_t* xraw = xs + (((kXSlot * G + n_out) + 7) & ~7);  // 16-byte aligned
+  uint16_t* xraw = xs + MX * xstride;
   const int tid = threadIdx.x;
   const int lt = tid % L;
   const int team = tid / L;
@@ -357,19 +440,21 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   // The first tile's weights are requested right behind the x and perm
   // loads, so their HBM latency overlaps the gather and the barriers.
   Frag<P, U, OS> fa, fb;
-  stage_x(v, task.x, xs, xraw, tid, [&] {
+  stage_x<MX>(v, task.x, tasks.m_rows, xs, xstride, xraw, tid, [&] {
     __builtin_amdgcn_sched_barrier(0);
     load_frag<L, P, U, OS>(fa, v, row, end, lt, team);
     __builtin_amdgcn_sched_barrier(0);
   });
   __syncthreads();
 
-  float xor_[OS];
+  float xor_[MX][OS];
 #pragma unroll
-  for (int s = 0; s < OS; ++s) {
-    const int j = lt + L * s;
-    xor_[s] = j < n_out ? h2f(xo[j]) : 0.f;
-  }
+  for (int m = 0; m < MX; ++m)
+#pragma unroll
+    for (int s = 0; s < OS; ++s) {
+      const int j = lt + L * s;
+      xor_[m][s] = j < n_out ? h2f(xs[m * xstride + kXSlot * G + j]) : 0.f;
+    }
   // Two register buffers: the next tile is in flight while this one is
   // computed.  Neither form has an early exit between a load and the compute
   // that uses it (a tile past `end` loads nothing and its compute is skipped
@@ -385,16 +470,16 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
       if (t + 1 < NT) load_frag<L, P, U, OS>(nxt, v, row + (t + 1) * stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
       if (row + t * stride < end)
-        compute_frag<L, P, U, OS>(cur, v, row + t * stride, end, lt, team, xs, xor_, xo, task.y, nb);
+        compute_frag<L, P, U, OS, MX>(cur, v, row + t * stride, end, lt, team, xs, xstride, xor_, tasks.m_rows, task.y, nb);
     }
   } else {
     for (; row < v.N; row += 2 * stride) {
       load_frag<L, P, U, OS>(fb, v, row + stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      compute_frag<L, P, U, OS>(fa, v, row, end, lt, team, xs, xor_, xo, task.y, nb);
+      compute_frag<L, P, U, OS, MX>(fa, v, row, end, lt, team, xs, xstride, xor_, tasks.m_rows, task.y, nb);
       load_frag<L, P, U, OS>(fa, v, row + 2 * stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      if (row + stride < v.N) compute_frag<L, P, U, OS>(fb, v, row + stride, end, lt, team, xs, xor_, xo, task.y, nb);
+      if (row + stride < v.N) compute_frag<L, P, U, OS, MX>(fb, v, row + stride, end, lt, team, xs, xstride, xor_, tasks.m_rows, task.y, nb);
     }
   }
 }
@@ -422,18 +507,26 @@ Variant pick_variant(int G) {
   return best;
 }
 
-size_t lds_bytes(const DeviceView& v) {
-  return 2 * ((((size_t)kXSlot * v.G + (size_t)v.n_out) + 7) & ~(size_t)7) +
-         16 * (((size_t)v.K + 7) / 8);
+// LDS of one block: MX rows of x in group slots, plus the raw x of one row.
+size_t lds_bytes(const DeviceView& v, int mx) {
+  const size_t xstride = (((size_t)kXSlot * v.G + (size_t)v.n_out) + 7) & ~(size_t)7;
+  return 2 * (size_t)mx * xstride + 16 * (((size_t)v.K + 7) / 8);
 }
 
+size_t lds_limit(const DeviceView& v) {
+  const size_t dev = v.lds_per_block > 0 ? (size_t)v.lds_per_block : 64 * 1024;
+  return dev < (size_t)160 * 1024 ? dev : (size_t)160 * 1024;
+}
+
+// Rows of x one launch carries: M = 1, 2 or up to 4 (rows past M read zeros).
+int batch_tile(int64_t M) { return M <= 1 ? 1 : (M == 2 ? 2 : 4); }
+
 constexpr int kU = SPECTRA_GEMV_U;
-constexpr size_t kMaxLds = 64 * 1024;
 constexpr int64_t kPipeTiles = 6;  // tiles per block from which the loop without early exits pays
 
 // Split the block budget between the tasks in proportion to their rows.
-template <int L, int P>
-int64_t plan_blocks(GemvTasks& ts) {
+template <int L, int P, int MX>
+int64_t plan_blocks(GemvTasks& ts, size_t lds) {
   constexpr int64_t kTileRows = (int64_t)(kBlock / L) * kU;
   int64_t total_rows = 0;
   for (int i = 0; i < ts.count; ++i) total_rows += ts.t[i].v.N;
@@ -441,12 +534,14 @@ int64_t plan_blocks(GemvTasks& ts) {
   // per CU (16 waves, so one wave's dequant work overlaps another's loads);
   // short ones keep one block, whose x staging is then paid once per CU.
   // Two blocks fit only while a lane needs at most 128 registers, which
-  // holds up to four slots per lane.
+  // holds for one row of x and up to four slots per lane, and the LDS of
+  // two blocks fits the CU's 160 KiB.
   int64_t all_tiles = 0;
   for (int i = 0; i < ts.count; ++i) all_tiles += (ts.t[i].v.N + kTileRows - 1) / kTileRows;
   const int64_t cus = ts.t[0].v.cu_count;
-  const int64_t bpc = (P <= 4 && all_tiles >= cus * 2 * SPECTRA_GEMV_TWO_BLOCK_TILES) ? 2 : SPECTRA_GEMV_BLOCKS_PER_CU;
-  const int64_t budget = cus * bpc;
+  const bool two = MX == 1 && P <= 4 && 2 * lds <= (size_t)160 * 1024 &&
+                   all_tiles >= cus * 2 * SPECTRA_GEMV_TWO_BLOCK_TILES;
+  const int64_t budget = cus * (two ? 2 : SPECTRA_GEMV_BLOCKS_PER_CU);
   int64_t begin = 0;
   for (int i = 0; i < ts.count; ++i) {
     GemvTask& t = ts.t[i];
@@ -461,21 +556,31 @@ int64_t plan_blocks(GemvTasks& ts) {
   return begin;
 }
 
-template <int L, int P>
+template <int L, int P, int NT, int MX>
+hipError_t launch_k(dim3 grid, size_t lds, hipStream_t s, const GemvTasks& ts) {
+  const void* fn = reinterpret_cast<const void*>(&k_gemv_m1<L, P, kU, NT, MX>);
+  if (lds > 64 * 1024) {  // dynamic LDS past 64 KiB must be allowed per kernel
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_gemv_m1<L, P, kU, NT, MX>), grid, dim3(kBlock), lds, s, ts);
+  return hipGetLastError();
+}
+
+template <int L, int P, int MX>
 hipError_t launch_lp(GemvTasks& ts, size_t lds, hipStream_t s) {
   constexpr int64_t kTileRows = (int64_t)(kBlock / L) * kU;
-  const int64_t blocks = plan_blocks<L, P>(ts);
+  const int64_t blocks = plan_blocks<L, P, MX>(ts, lds);
   int64_t most = 0;  // most tiles any block walks when blocks take whole tiles in turn
   for (int i = 0; i < ts.count; ++i) {
     const int64_t tiles = (ts.t[i].v.N + kTileRows - 1) / kTileRows;
     const int64_t per = (tiles + ts.t[i].nblocks - 1) / ts.t[i].nblocks;
     most = per > most ? per : most;
   }
-  const dim3 grid((unsigned)blocks), block(kBlock);
-  if (most >= kPipeTiles) {
+  const dim3 grid((unsigned)blocks);
+  if (MX > 1 || most >= kPipeTiles) {  // batch tiles always take the loop form
     for (int i = 0; i < ts.count; ++i) ts.t[i].rows_per_block = 0;
-    hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 0>), grid, block, lds, s, ts);
-    return hipGetLastError();
+    return launch_k<L, P, 0, MX>(grid, lds, s, ts);
   }
   // Short launch: equal row ranges per block, at most nt tiles each.
   int64_t nt = 1;
@@ -486,59 +591,84 @@ hipError_t launch_lp(GemvTasks& ts, size_t lds, hipStream_t s) {
     nt = t > nt ? t : nt;
   }
   switch (nt) {
-    case 1: hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 1>), grid, block, lds, s, ts); break;
-    case 2: hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 2>), grid, block, lds, s, ts); break;
-    case 3: hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 3>), grid, block, lds, s, ts); break;
-    case 4: hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 4>), grid, block, lds, s, ts); break;
-    default: hipLaunchKernelGGL((k_gemv_m1<L, P, kU, 5>), grid, block, lds, s, ts); break;
+    case 1: return launch_k<L, P, 1, 1>(grid, lds, s, ts);
+    case 2: return launch_k<L, P, 2, 1>(grid, lds, s, ts);
+    case 3: return launch_k<L, P, 3, 1>(grid, lds, s, ts);
+    case 4: return launch_k<L, P, 4, 1>(grid, lds, s, ts);
+    default: return launch_k<L, P, 5, 1>(grid, lds, s, ts);
   }
-  return hipGetLastError();
 }
 
-template <int L>
+// Most slots per lane a batch tile of MX rows of x runs without spilling registers.
+constexpr int max_slots(int mx) { return mx >= 4 ? 4 : 8; }
+
+template <int L, int MX>
 hipError_t launch_l(int P, GemvTasks& ts, size_t lds, hipStream_t s) {
-  switch (P) {
-    case 1: return launch_lp<L, 1>(ts, lds, s);
-    case 2: return launch_lp<L, 2>(ts, lds, s);
-    case 3: return launch_lp<L, 3>(ts, lds, s);
-    case 4: return launch_lp<L, 4>(ts, lds, s);
-    case 5: return launch_lp<L, 5>(ts, lds, s);
-    case 6: return launch_lp<L, 6>(ts, lds, s);
-    case 7: return launch_lp<L, 7>(ts, lds, s);
-    case 8: return launch_lp<L, 8>(ts, lds, s);
-    default: return hipErrorNotSupported;
+  if constexpr (max_slots(MX) < 8) {
+    switch (P) {
+      case 1: return launch_lp<L, 1, MX>(ts, lds, s);
+      case 2: return launch_lp<L, 2, MX>(ts, lds, s);
+      case 3: return launch_lp<L, 3, MX>(ts, lds, s);
+      case 4: return launch_lp<L, 4, MX>(ts, lds, s);
+      default: return hipErrorNotSupported;
+    }
+  } else {
+    switch (P) {
+      case 1: return launch_lp<L, 1, MX>(ts, lds, s);
+      case 2: return launch_lp<L, 2, MX>(ts, lds, s);
+      case 3: return launch_lp<L, 3, MX>(ts, lds, s);
+      case 4: return launch_lp<L, 4, MX>(ts, lds, s);
+      case 5: return launch_lp<L, 5, MX>(ts, lds, s);
+      case 6: return launch_lp<L, 6, MX>(ts, lds, s);
+      case 7: return launch_lp<L, 7, MX>(ts, lds, s);
+      case 8: return launch_lp<L, 8, MX>(ts, lds, s);
+      default: return hipErrorNotSupported;
+    }
   }
 }
 
-hipError_t launch_tasks(GemvTasks& ts, hipStream_t s) {
+template <int MX>
+hipError_t launch_mx(int L, int P, GemvTasks& ts, size_t lds, hipStream_t s) {
+  switch (L) {
+    case 16: return launch_l<16, MX>(P, ts, lds, s);
+    case 32: return launch_l<32, MX>(P, ts, lds, s);
+    default: return launch_l<64, MX>(P, ts, lds, s);
+  }
+}
+
+hipError_t launch_tasks(GemvTasks& ts, int64_t M, hipStream_t s) {
   ts.nib_lo = 0x000F000Fu;
   ts.nib_hi = 0x00F000F0u;
   ts.mag_lo = 0x64006400u;
   ts.mag_hi = 0x54005400u;
+  ts.m_rows = (int32_t)M;
+  const int mx = batch_tile(M);
   int gmax = 0;
   size_t lds = 0;
   for (int i = 0; i < ts.count; ++i) {
     if (ts.t[i].v.G > gmax) gmax = ts.t[i].v.G;
-    const size_t b = lds_bytes(ts.t[i].v);
+    const size_t b = lds_bytes(ts.t[i].v, mx);
     if (b > lds) lds = b;
   }
   const Variant vr = pick_variant(gmax);
-  if (vr.P == 0 || lds > kMaxLds) return hipErrorNotSupported;
-  switch (vr.L) {
-    case 16: return launch_l<16>(vr.P, ts, lds, s);
-    case 32: return launch_l<32>(vr.P, ts, lds, s);
-    default: return launch_l<64>(vr.P, ts, lds, s);
+  if (vr.P == 0 || lds > lds_limit(ts.t[0].v)) return hipErrorNotSupported;
+  switch (mx) {
+    case 1: return launch_mx<1>(vr.L, vr.P, ts, lds, s);
+    case 2: return launch_mx<2>(vr.L, vr.P, ts, lds, s);
+    default: return launch_mx<4>(vr.L, vr.P, ts, lds, s);
   }
 }
 
 }  // namespace
 
 bool gemv_supports(const DeviceView& v, int64_t M) {
-  if (M != 1) return false;
+  if (M < 1 || M > 4) return false;
+  if (M > 1 && v.K % 8 != 0) return false;  // each row of x must start 16-byte aligned
   // a block stages at most kXChunks * 8 * kBlock channels and kQuads * 4 * kBlock bulk positions
   if (v.K > kXChunks * 8 * kBlock || (int64_t)kGroup * v.G > (int64_t)kQuads * 4 * kBlock) return false;
-  if (pick_variant(v.G).P == 0) return false;
-  return lds_bytes(v) <= kMaxLds;
+  const int P = pick_variant(v.G).P;
+  if (P == 0 || P > max_slots(batch_tile(M))) return false;
+  return lds_bytes(v, batch_tile(M)) <= lds_limit(v);
 }
 
 hipError_t launch_gemv(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M,
@@ -549,7 +679,7 @@ hipError_t launch_gemv(const DeviceView& v, const uint16_t* x, uint16_t* y, int6
   ts.t[0].v = v;
   ts.t[0].x = x;
   ts.t[0].y = y;
-  return launch_tasks(ts, s);
+  return launch_tasks(ts, M, s);
 }
 
 hipError_t launch_gemv_grouped(const DeviceView* vs, int count, const uint16_t* x,
@@ -563,7 +693,7 @@ hipError_t launch_gemv_grouped(const DeviceView* vs, int count, const uint16_t* 
       ts.t[i].x = x;
       ts.t[i].y = ys[base + i];
     }
-    const hipError_t e = launch_tasks(ts, s);
+    const hipError_t e = launch_tasks(ts, 1, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

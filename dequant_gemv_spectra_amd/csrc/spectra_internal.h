@@ -51,6 +51,7 @@ struct DeviceView {
   int64_t N;
   int32_t K, K_b, G, n_out;
   int32_t cu_count;          // compute units of the container's device (launch sizing)
+  int32_t lds_per_block;     // LDS bytes one block may use on that device
 };
 
 // Per-device properties the launchers need.
@@ -82,6 +83,7 @@ struct spectra_container {
     v.G = (int32_t)G;
     v.n_out = (int32_t)n_out;
     v.cu_count = spectra::device_props(device).cu_count;
+    v.lds_per_block = (int32_t)spectra::device_props(device).lds_per_block;
     return v;
   }
 };

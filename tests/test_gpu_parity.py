@@ -308,6 +308,68 @@ def test_grouped_launch_matches_single_launches():
         check_product(c, img, x)
 
 
+GEMV_BATCH = [  # (N, K, planted heavy-tailed channels, seed, M): the GEMV with 2 or 4 rows of x
+    (64, 2048, 20, 51, 2),    # one slot per lane
+    (100, 4096, 40, 52, 3),   # M = 3 in a 4-row batch tile (the fourth row reads zeros)
+    (257, 8192, 82, 54, 4),   # four slots per lane, ragged last tile
+    (33, 1000, 10, 55, 2),    # K % 32 != 0
+    (50, 3072, 31, 56, 4),    # 32-lane teams
+    (700, 2560, 30, 58, 2),   # 16-lane teams, five slots per lane
+]
+
+
+@pytest.mark.parametrize("N,K,n_out,seed,M", GEMV_BATCH)
+def test_gemv_batch_rows(N, K, n_out, seed, M):
+    W, g, x = synth.random_case(N, K, n_out, seed, M=M)
+    c, img = check_pack(W, g)
+    check_product(c, img, x, kernel="gemv")
+    check_product(c, img, x)  # auto picks the GEMV for M <= 4
+
+
+def test_gemv_batch_declines():
+    """Four rows need at most four slots per lane (else registers spill) and
+    every row of x 16-byte aligned (K % 8 == 0): otherwise the GEMV declines
+    and auto takes the MFMA path."""
+    sp, torch = _sp(), _torch()
+    for N, K, n_out, seed, M in [(300, 2560, 25, 53, 4), (17, 1004, 3, 57, 2)]:
+        W, g, x = synth.random_case(N, K, n_out, seed, M=M)
+        c, img = check_pack(W, g)
+        check_product(c, img, x)
+        with pytest.raises(sp.SpectraError) as ei:
+            sp.spectra_gemm(c, torch.from_numpy(x).cuda(), kernel="gemv")
+        assert ei.value.status == sp.SPECTRA_E_UNSUPPORTED
+
+
+def test_gemv_batch_large_lds():
+    """Two rows of x at K = 12288 need about 86 KiB of LDS per block: the
+    GEMV runs it where the device allows that much, else declines."""
+    sp = _sp()
+    W, g, x = synth.random_case(40, 12288, 120, 59, M=2)
+    c, img = check_pack(W, g)
+    check_product(c, img, x)
+    try:
+        check_product(c, img, x, kernel="gemv")
+    except sp.SpectraError as e:
+        assert e.status == sp.SPECTRA_E_UNSUPPORTED
+        print("GEMV declined two rows at K = 12288 (LDS limit of this device)")
+
+
+def test_gemv_batch_one_hot_exact():
+    sp, torch = _sp(), _torch()
+    W, g, _ = synth.random_case(200, 304, 6, 60)
+    W[:, 11] = (np.random.default_rng(3).standard_t(3, 200) * 0.2).astype(np.float16)
+    c, img = check_pack(W, g)
+    u = O.unpack(img)
+    ks = list(u["perm"][u["K_b"]:][:2]) + [int(u["perm"][0]), int(u["perm"][u["K_b"] - 1])]
+    x = np.zeros((4, 304), np.float16)
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    for M in (2, 3, 4):
+        y = sp.spectra_gemm(c, torch.from_numpy(x[:M].copy()).cuda(), kernel="gemv").cpu().numpy()
+        for i, k in enumerate(ks[:M]):
+            assert np.array_equal(y[i], u["W_hat"][:, k].astype(np.float16)), (M, k)
+
+
 MFMA_CASES = [  # (N, K, planted heavy-tailed channels, seed, M)
     (64, 200, 9, 31, 2), (100, 1000, 10, 32, 3), (129, 2088, 40, 33, 16), (300, 96, 3, 34, 17),
     (65, 4096, 40, 35, 33), (257, 2560, 30, 36, 70), (128, 8192, 82, 37, 128), (77, 512, 0, 38, 130),
@@ -319,7 +381,7 @@ MFMA_CASES = [  # (N, K, planted heavy-tailed channels, seed, M)
 def test_mfma_product_small(N, K, n_out, seed, M):
     W, g, x = synth.random_case(N, K, n_out, seed, M=M)
     c, img = check_pack(W, g)
-    check_product(c, img, x)                   # auto: the MFMA path for M >= 2
+    check_product(c, img, x)                   # auto: the MFMA path for M >= 5 (and shapes the GEMV declines)
     check_product(c, img, x, kernel="mfma")
 
 
@@ -359,3 +421,5 @@ def test_config_large_batched(cfg):
             continue
         x = synth.activations(lin, cfg, M)
         check_product(c, img, x, rows=rows)
+        if M <= 4:  # auto ran the GEMV: the MFMA path at the same M too
+            check_product(c, img, x, rows=rows, kernel="mfma")
