@@ -545,9 +545,10 @@ int64_t plan_blocks(GemvTasks& ts, size_t lds) {
   int64_t begin = 0;
   for (int i = 0; i < ts.count; ++i) {
     GemvTask& t = ts.t[i];
-    const int64_t tiles = (t.v.N + kTileRows - 1) / kTileRows;
+    // more blocks than whole tiles is fine: short launches then give every
+    // block a partial tile (rows_per_block below kTileRows)
     int64_t blocks = (budget * t.v.N + total_rows - 1) / total_rows;
-    if (blocks > tiles) blocks = tiles;
+    if (blocks > t.v.N) blocks = t.v.N;
     if (blocks < 1) blocks = 1;
     t.block_begin = (int32_t)begin;
     t.nblocks = (int32_t)blocks;

@@ -1,5 +1,5 @@
-// SPECTRA batched product for gfx950: y = x W_hat^T for M >= 2 on the matrix
-// cores (v_mfma_f32_16x16x32_f16).
+// SPECTRA batched product for gfx950: y = x W_hat^T on the matrix cores
+// (v_mfma_f32_16x16x32_f16), for M >= 5 and the shapes the GEMV declines.
 //
 // The SPECTRA page reports Tensor-Core prefill next to its decode kernels
 // (highlight 4); this is the gfx950 counterpart for batched rows, written for
@@ -9,20 +9,19 @@
 // bulk order, zero padded to 32G, followed by the heavy-tailed x values
 // zero padded to a multiple of 32.
 //
-// Pass 2 (k_mfma): the weights never pass through LDS.  A wave owns 16 * NT
-// consecutive output rows for the whole K loop and, per chunk of 4 groups,
-// loads one 16-byte code record per lane and 16-row tile: lane (r, c) takes
-// the record of row c, group g0 + r.  Two permlane32 and two permlane16 swaps
-// transpose those 4 x 4 dwords so that lane (r, c) holds, for group g0 + j,
-// dword r of row c's record: members 8r .. 8r + 7, which is exactly the B
-// operand of v_mfma_f32_16x16x32_f16 for that group.  The dword is
+// Pass 2 (k_mfma): a wave owns 16 * NT consecutive output rows for the whole
+// K loop.  Per chunk of CG groups it loads its code records row-contiguously
+// (consecutive lanes on consecutive records of a row: whole cache lines),
+// stores them to a small wave-private LDS tile and reads them back in the
+// B-operand order of v_mfma_f32_16x16x32_f16: lane (r, c) takes dword r of
+// row c's record, members 8r .. 8r + 7 of the group.  The dword is
 // dequantized in registers to exact fp16 (q - z): (w & 0x000F000F) | 0x6400
 // 6400 holds 1024 + q of two members, (w & 0x00F000F0) | 0x5400 5400 holds
 // 64 + q of the next two, and subtracting 1024 + z or 64 + z is exact.  One
 // MFMA per group and m-subtile into a zero accumulator, then acc += s16 * D in
 // fp32, so the weights are never rounded a second time.  The A operand (x in
-// bulk order, 16*MT rows x 128 positions per chunk) is staged in LDS once per
-// block and chunk; the weights run kDepth chunks ahead in registers.  The
+// bulk order, 16*MT rows x 32*CG positions per chunk) is staged in LDS once per
+// block and chunk; the weights run 4 chunks ahead in registers.  The
 // heavy-tailed columns follow as plain MFMA steps (fp16 weights, scale 1).
 // Loads use buffer descriptors: rows past N or M and positions past the
 // padded K read as zero.
