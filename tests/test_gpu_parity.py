@@ -115,7 +115,8 @@ def test_pack_bitexact_and_product_small(N, K, n_out, seed):
 
 GEMV_EDGE = [  # (N, K, planted heavy-tailed channels, seed): x-staging edge cases of the GEMV
     (50, 12288, 120, 16),  # K % 8 == 0, 384 groups per row
-    (40, 14000, 100, 21),  # x slots close to the 64 KiB LDS limit, 7 groups per lane
+    (40, 14000, 100, 21),  # 7 groups per lane, 62 KiB of LDS
+    (24, 15000, 100, 22),  # 66 KiB of LDS: past 64 KiB, enabled per kernel
     (20, 12287, 0, 17),    # K % 8 == 7 at the limit (short columns: kurtosis flags some anyway)
     (37, 7777, 20, 18),    # K % 8 == 1: a partial last x chunk
     (3, 8191, 64, 19),     # K % 8 == 7, three rows
@@ -131,10 +132,10 @@ def test_gemv_staging_edges(N, K, n_out, seed):
 
 
 def test_gemv_beyond_staging_limit_falls_back():
-    """x staged in bulk order needs more than 64 KiB of LDS (K = 15000): the
-    GEMV declines, auto takes the MFMA path."""
+    """K = 17000 is past the 16384 channels one block stages: the GEMV
+    declines, auto takes the MFMA path."""
     sp, torch = _sp(), _torch()
-    W, g, x = synth.random_case(24, 15000, 100, 25)
+    W, g, x = synth.random_case(24, 17000, 100, 25)
     c, img = check_pack(W, g)
     check_product(c, img, x)  # auto
     with pytest.raises(sp.SpectraError) as ei:
