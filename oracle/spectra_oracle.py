@@ -41,6 +41,9 @@ Parity status of each function (what pins it, in tests/test_oracle_pins.py):
   matmul_ref         pure-Python brute force on tiny shapes, one-hot inputs
   tolerance          definition written in the header; no independent pin
                      beyond its use (parity unpinned as a formula)
+  embed_ref          grid-valued tables gather back bit-exact (bulk and
+                     heavy-tailed channels), pure-Python brute force over the
+                     unpacked fields, out-of-range ids give zero rows
 """
 from __future__ import annotations
 
@@ -342,3 +345,29 @@ def reconstruct_rows(img: bytes, rows: np.ndarray) -> np.ndarray:
     W_hat[:, perm[:K_b]] = dequantize_groups(q, z, s16, K_b)
     W_hat[:, perm[K_b:]] = O.astype(np.float64)
     return W_hat
+
+
+# ---------------------------------------------------------------------------
+# Step 6: row gather (the fused embedding)
+# ---------------------------------------------------------------------------
+def embed_ref(img: bytes, ids) -> np.ndarray:
+    """Rows W_hat[ids[i]] in channel order, each entry rounded once to fp16
+    (round to nearest even); an id outside [0, N) gives a row of zeros.
+
+    SPECTRA page ("SPECTRA: Sparse-Precision Exact Channel Tensor
+    Reconstruction Architecture", abstract and highlight 5, the fused
+    embedding): a vocabulary table is kept in the same Group-32 4-bit format
+    and the rows a forward pass needs are gathered and dequantized on the fly.
+    Reading: the table E [V][D] is packed as W with N = V rows and K = D
+    channels, and a gathered row is that row of W_hat (bulk entries
+    (q - z) * s16, heavy-tailed entries their fp16 bits).  The bulk value is
+    exact in binary64, so one rounding to fp16 is the only one.
+    """
+    hdr = np.frombuffer(img, dtype="<u8", count=HEADER_BYTES // 8)
+    K, N = int(hdr[1]), int(hdr[2])
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    ok = (ids >= 0) & (ids < N)
+    out = np.zeros((ids.size, K), dtype=np.float16)
+    if ok.any():
+        out[ok] = reconstruct_rows(img, ids[ok]).astype(np.float16)
+    return out

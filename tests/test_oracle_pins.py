@@ -338,3 +338,53 @@ def test_tolerance_definition_shape_and_floor():
     t = O.tolerance(W_hat, x)
     assert t.shape == (1, 2)
     assert t[0, 0] == pytest.approx(1e-3 * 5 + 1e-6) and t[0, 1] == pytest.approx(1e-6)
+
+
+# --------------------------------------------------------------------------
+# row gather (fused embedding)
+# --------------------------------------------------------------------------
+def _grid_table(N, K, spike_ch, e, seed):
+    """A table whose bulk groups are grid-valued (codes 0 and 15 present in
+    every row and group, scale 2^e) and whose channel spike_ch is a single
+    spike (flagged heavy-tailed for N >= 8): the gather must return it
+    bit-exactly."""
+    rng = np.random.default_rng(seed)
+    bulk = [k for k in range(K) if k != spike_ch]
+    W = np.zeros((N, K), np.float64)
+    for n in range(N):
+        for g0 in range(0, len(bulk), 32):
+            chans = bulk[g0:g0 + 32]
+            z = int(rng.integers(0, 16))
+            q = rng.integers(0, 16, len(chans))
+            q[rng.choice(len(chans), 2, replace=False)] = [0, 15]
+            W[n, chans] = (q - z) * 2.0 ** e
+    W[3, spike_ch] = 1.5
+    W16 = W.astype(np.float16)
+    assert np.array_equal(W16.astype(np.float64), W)
+    return W16
+
+
+@pytest.mark.parametrize("N,K,spike,e,seed", [(40, 65, 5, -6, 0), (24, 97, 96, -10, 1), (64, 33, 0, -3, 2)])
+def test_embed_ref_grid_table_is_exact(N, K, spike, e, seed):
+    W = _grid_table(N, K, spike, e, seed)
+    img = O.pack(W, np.ones(K, np.float16))
+    u = O.unpack(img)
+    assert u["mask"][spike] and u["n_out"] == 1
+    ids = np.array([0, 3, N - 1, 3, 7 % N])
+    out = O.embed_ref(img, ids)
+    assert out.dtype == np.float16
+    assert np.array_equal(out.view(np.uint16), W[ids].view(np.uint16))
+
+
+def test_embed_ref_out_of_range_rows_are_zero_and_match_unpack():
+    W, g, _ = synth.random_case(30, 70, 3, 11)
+    img = O.pack(W, g)
+    ids = np.array([-1, 0, 29, 30, 12, 12, 1 << 40])
+    out = O.embed_ref(img, ids)
+    ref = O.unpack(img)["W_hat"].astype(np.float16)
+    for i, t in enumerate(ids):
+        if 0 <= t < 30:
+            assert np.array_equal(out[i].view(np.uint16), ref[t].view(np.uint16))
+        else:
+            assert not out[i].any()
+    assert O.embed_ref(img, np.zeros(0, np.int64)).shape == (0, 70)
