@@ -17,7 +17,10 @@ grouped launch counts x once).
 
 Other workloads: cfg1 / cfg4 / cfg5 time one linear per step, rotating over
 enough distinct packed copies to exceed 1 GiB so the last-level cache cannot
-serve the weights; cfg2 stacks the 1.5B-class layer 28 deep.
+serve the weights; cfg2 stacks the 1.5B-class layer 28 deep.  `embed` times
+the fused embedding gather instead (its own metric): --tokens random rows of
+the 131072 x 3072 table per step, rotated over copies the same way; bytes =
+the gathered rows' payload + the fp16 rows written + the ids.
 
 Prints ONE JSON line.  roofline: the dominant kernel (largest share of step
 bytes) is replayed alone as a captured graph and timed with HIP events on its
@@ -46,7 +49,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="cfg3", choices=["cfg1", "cfg2", "cfg3", "cfg4", "cfg5"])
+    ap.add_argument("--workload", default="cfg3", choices=["cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "embed"])
+    ap.add_argument("--tokens", type=int, default=16384, help="embed: token ids gathered per step")
     ap.add_argument("--M", type=int, default=1)
     ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "mfma"])
     ap.add_argument("--layers", type=int, default=None, help="cfg3: fewer layers (quick runs)")
@@ -63,9 +67,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha():
+def kernel_sources_sha(files=("gemv.hip", "mfma.hip", "spectra_internal.h")):
     h = hashlib.sha256()
-    for f in ("gemv.hip", "mfma.hip", "spectra_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "dequant_gemv_spectra_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -153,6 +157,78 @@ def build_units(args, sp, torch):
     return wl.name, units, False
 
 
+EMBED_METRIC = "fused G32 embedding row gather: effective HBM GB/s (table rows read + fp16 rows written)"
+
+
+def run_embed(args, sp, torch):
+    """One step = gather args.tokens random rows of the 131072 x 3072 table
+    (the LM-head shape read as a tied embedding), rotating over distinct
+    packed copies (>= 1 GiB) so the rows come from HBM."""
+    import numpy as np
+    from dequant_gemv_spectra_amd import synth
+    cfg = 4
+    lin = synth.workload(cfg).linears[0]
+    W, g = synth.weights(lin, cfg), synth.gamma(lin, cfg)
+    first = sp.spectra_pack(W, g)
+    info = first.info()
+    copies = max(1, int(args.rotate_gib * 2 ** 30 // info["bytes_total"]) + 1)
+    cs = [first] + [sp.spectra_pack(W, g) for _ in range(1, copies)]
+    T = args.tokens
+    rng = np.random.default_rng(2024)
+    ids = [torch.from_numpy(rng.integers(0, lin.N, T).astype(np.int32)).cuda() for _ in cs]
+    outs = [torch.empty((T, lin.K), dtype=torch.float16, device="cuda") for _ in cs]
+    row_bytes = (info["bytes_payload"]) / lin.N  # codes + scales + zeros + fp16 channels of one row
+    step_bytes = T * (row_bytes + 2 * lin.K + 4)
+    log(f"embed: {copies} distinct copies of {lin.N} x {lin.K}, {T} ids per step, "
+        f"{step_bytes / 1e6:.1f} MB per step")
+
+    def mk(c, i, o):
+        def f():
+            sp.spectra_embed(c, i, out=o)
+        return f
+    fns = [mk(c, i, o) for c, i, o in zip(cs, ids, outs)]
+    graph = capture(torch, fns)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // len(fns))
+    ms = time_graph(torch, graph, reps) / len(fns)
+    value = step_bytes / (ms * 1e-3) / 1e9
+    dgraph = capture(torch, fns)
+    dgraph.replay()
+    dms = time_graph(torch, dgraph, 10) / len(fns)
+    achieved = step_bytes / (dms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "k_embed", "avg_launch_us": round(dms * 1e3, 3),
+                "bytes_per_launch": int(step_bytes), "launches_timed": 10 * len(fns)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import spectra_oracle as O
+        img = sp.spectra_export(first)
+        sample = rng.integers(0, lin.N, 2048)
+        done, t_total, rounds = 0, 0.0, 0
+        while t_total < 10.0:
+            t0 = time.perf_counter()
+            O.embed_ref(img, sample)
+            t_total += time.perf_counter() - t0
+            done += sample.size
+            rounds += 1
+        cpu = {"value": round(done * (row_bytes + 2 * lin.K + 4) / t_total / 1e9, 4), "unit": "GB/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"oracle row gather (unpack of the sampled rows + fp16 rounding) of 2048 random ids "
+                         f"x {rounds} rounds in {t_total:.1f} s; single-threaded numpy"}
+    out = {"metric": EMBED_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+           "data": "synthetic",
+           "config": {"workload": f"embedding-gather-{lin.N}x{lin.K}", "tokens": T,
+                      "bytes_per_step": int(step_bytes), "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+                      "hip_graph": True, "parallelism": "single GPU"},
+           "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
 _CAPTURE_STREAM = None
 
 
@@ -236,6 +312,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": a.numel() * 2, "written": b.numel() * 2, "copies": 5}))
+        return
+    if args.workload == "embed":
+        run_embed(args, sp, torch)
         return
     cfg = int(args.workload[3:])
     t0 = time.time()

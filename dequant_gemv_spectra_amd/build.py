@@ -26,6 +26,7 @@ SOURCES = {
     "pack.hip": ["-ffp-contract=off"],
     "gemv.hip": [],
     "mfma.hip": [],
+    "embed.hip": [],
 }
 
 COMMON = [

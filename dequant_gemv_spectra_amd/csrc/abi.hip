@@ -383,4 +383,19 @@ int spectra_gemm_grouped(const spectra_container* const* cs, int count, const vo
   return SPECTRA_OK;
 }
 
+int spectra_embed(const spectra_container* c, const void* ids, int64_t T, void* out, void* stream) {
+  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+  if (T < 0 || T > SPECTRA_MAX_T) return fail(SPECTRA_E_INVAL, "T out of range [0, 2^31]");
+  if (T == 0) return SPECTRA_OK;
+  if (!ids || !out) return fail(SPECTRA_E_INVAL, "null ids or out");
+  if ((reinterpret_cast<uintptr_t>(ids) & 3) || (reinterpret_cast<uintptr_t>(out) & 3))
+    return fail(SPECTRA_E_INVAL, "ids and out must be 4-byte aligned");
+  const DeviceView v = c->view();
+  if (!embed_supports(v)) return fail(SPECTRA_E_UNSUPPORTED, "row gather: a row does not fit the LDS row buffer");
+  const hipError_t e = launch_embed(v, static_cast<const int32_t*>(ids), T, static_cast<uint16_t*>(out),
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("row gather launch", e));
+  return SPECTRA_OK;
+}
+
 }  // extern "C"

@@ -116,6 +116,11 @@ size_t mfma_workspace_bytes(const DeviceView& v, int64_t M);
 hipError_t launch_mfma_ws(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M,
                           void* workspace, hipStream_t s);
 
+// ---- row gather (embed.hip) ----
+bool embed_supports(const DeviceView& v);
+hipError_t launch_embed(const DeviceView& v, const int32_t* ids, int64_t T, uint16_t* out,
+                        hipStream_t s);
+
 // ---- per-stream workspace (abi.hip) ----
 // A device buffer of at least `bytes` reserved for work enqueued on stream s
 // of `device`; grown on demand (growth waits for s and reallocates).

@@ -24,8 +24,8 @@ SPECTRA_E_UNSUPPORTED = -5
 KERNELS = {"auto": 0, "gemv": 1, "mfma": 2}
 
 EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm_ex",
-            "spectra_gemm_grouped", "spectra_free", "spectra_info", "spectra_export",
-            "spectra_last_error", "spectra_version"]
+            "spectra_gemm_grouped", "spectra_embed", "spectra_free", "spectra_info",
+            "spectra_export", "spectra_last_error", "spectra_version"]
 
 
 class SpectraError(RuntimeError):
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.spectra_gemm_ex.restype = c_int
     L.spectra_gemm_grouped.argtypes = [ctypes.POINTER(vp), c_int, vp, ctypes.POINTER(vp), i64, vp]
     L.spectra_gemm_grouped.restype = c_int
+    L.spectra_embed.argtypes = [vp, vp, i64, vp, vp]
+    L.spectra_embed.restype = c_int
     L.spectra_free.argtypes = [vp]
     L.spectra_free.restype = None
     L.spectra_info.argtypes = [vp, ctypes.POINTER(spectra_info_t)]
@@ -193,6 +195,23 @@ def spectra_gemm_grouped(cs, x, ys=None, stream=None):
     _check(lib().spectra_gemm_grouped(arr_c, n, ctypes.c_void_p(x.data_ptr()), arr_y, x.shape[0],
                                       _stream_ptr(stream)))
     return ys
+
+
+def spectra_embed(c: Container, ids, out=None, stream=None):
+    """Rows of the packed table for CUDA int32 ids [T]: fp16 [T][K] (allocated if None)."""
+    import torch
+    info = c.info()
+    if ids.dtype != torch.int32 or not ids.is_cuda or ids.dim() != 1:
+        raise ValueError("ids must be a 1-D CUDA int32 tensor")
+    ids = ids.contiguous()
+    T = ids.shape[0]
+    if out is None:
+        out = torch.empty((T, info["K"]), dtype=torch.float16, device=ids.device)
+    elif out.dtype != torch.float16 or not out.is_contiguous() or tuple(out.shape) != (T, info["K"]):
+        raise ValueError("out must be a contiguous float16 tensor of shape [T][K]")
+    _check(lib().spectra_embed(c.handle, ctypes.c_void_p(ids.data_ptr()), T,
+                               ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+    return out
 
 
 def spectra_free(c: Container):

@@ -139,6 +139,7 @@ typedef struct {
 #define SPECTRA_MAX_K ((int64_t)1 << 24)
 #define SPECTRA_MAX_N ((int64_t)1 << 31)
 #define SPECTRA_MAX_M ((int64_t)1 << 20)
+#define SPECTRA_MAX_T ((int64_t)1 << 31)
 
 /* Pack W (HOST memory, [N][K] fp16 bits, row-major) with gain gamma (HOST
  * memory, [K] fp16 bits) into a new device-resident container on the current
@@ -175,6 +176,23 @@ int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t 
  * GEMV kernel; M must be 1. */
 int spectra_gemm_grouped(const spectra_container* const* cs, int count, const void* x,
                          void* const* ys, int64_t M, void* stream);
+
+/* Fused embedding gather (SPECTRA page, abstract and highlight 5: a
+ * vocabulary table kept in the Group-32 4-bit format, its rows dequantized
+ * as a forward pass gathers them).  The container holds the table E [V][D]
+ * packed as W with N = V rows and K = D channels.  For i < T:
+ *   out[i][k] = fp16(W_hat[ids[i]][k])  in channel order k < K,
+ * where W_hat's bulk entries are (q - z) * s16 (exact in fp32, rounded once
+ * to nearest even) and its heavy-tailed channels the stored fp16 bits; the
+ * result is bit-identical to dequantizing the row and rounding it to fp16.
+ * ids: DEVICE int32 [T]; out: DEVICE fp16 [T][K] contiguous, overwritten;
+ * both 4-byte aligned, on the container's device (16-byte aligned out with
+ * K % 8 == 0 takes whole-chunk stores).  An id outside [0, N) yields a row
+ * of zeros; nothing is read or written out of bounds.  0 <= T <= SPECTRA_MAX_T
+ * (T = 0 enqueues nothing).  Enqueued on `stream` (NULL = null stream);
+ * returns at once.  E_INVAL on bad arguments, E_UNSUPPORTED when one row
+ * does not fit the kernel's LDS row buffer (K above about 50000). */
+int spectra_embed(const spectra_container* c, const void* ids, int64_t T, void* out, void* stream);
 
 /* Release the container and its device memory.  NULL-safe; freeing a handle
  * twice, or one this library did not return, does nothing.  Handles are
