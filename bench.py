@@ -20,7 +20,8 @@ enough distinct packed copies to exceed 1 GiB so the last-level cache cannot
 serve the weights; cfg2 stacks the 1.5B-class layer 28 deep.  `embed` times
 the fused embedding gather instead (its own metric): --tokens random rows of
 the 131072 x 3072 table per step, rotated over copies the same way; bytes =
-the gathered rows' payload + the fp16 rows written + the ids.
+the gathered rows' payload + the fp16 rows written + the ids.  `load` times
+spectra_load of the 241 MB container file through the chunked staging path.
 
 Prints ONE JSON line.  roofline: the dominant kernel (largest share of step
 bytes) is replayed alone as a captured graph and timed with HIP events on its
@@ -49,8 +50,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="cfg3", choices=["cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "embed"])
+    ap.add_argument("--workload", default="cfg3", choices=["cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "embed", "load"])
     ap.add_argument("--tokens", type=int, default=16384, help="embed: token ids gathered per step")
+    ap.add_argument("--chunk-mib", type=int, default=8, help="load: staging chunk size")
     ap.add_argument("--M", type=int, default=1)
     ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "mfma"])
     ap.add_argument("--layers", type=int, default=None, help="cfg3: fewer layers (quick runs)")
@@ -229,6 +231,42 @@ def run_embed(args, sp, torch):
     print(json.dumps(out), flush=True)
 
 
+LOAD_METRIC = "container file streamed into HBM: GB/s (file bytes / wall time of spectra_load)"
+
+
+def run_load(args, sp, torch):
+    """One step = spectra_load of the 131072 x 3072 container (241 MB) from a
+    file written by spectra_save (the file sits in the page cache after the
+    save and the warmup loads: the rate is that of the staging path, not of a
+    disk).  Synchronous calls, timed by the host clock."""
+    import tempfile
+    from dequant_gemv_spectra_amd import synth
+    lin = synth.workload(4).linears[0]
+    c = sp.spectra_pack(synth.weights(lin, 4), synth.gamma(lin, 4))
+    total = c.info()["bytes_total"]
+    chunk = args.chunk_mib << 20
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "lm_head.spectra")
+        sp.spectra_save(c, path, chunk)
+        for _ in range(args.warmup):
+            sp.spectra_load(path, chunk).close()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            sp.spectra_load(path, chunk).close()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / max(1, args.steps)
+    value = total / (ms * 1e-3) / 1e9
+    out = {"metric": LOAD_METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bytes",
+           "data": "synthetic",
+           "config": {"workload": f"container-load-{lin.N}x{lin.K}", "bytes": int(total),
+                      "chunk_bytes": chunk, "peak_host_staging_bytes": 2 * chunk, "parallelism": "single GPU"},
+           "roofline": None, "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
 _CAPTURE_STREAM = None
 
 
@@ -315,6 +353,9 @@ def main():
         return
     if args.workload == "embed":
         run_embed(args, sp, torch)
+        return
+    if args.workload == "load":
+        run_load(args, sp, torch)
         return
     cfg = int(args.workload[3:])
     t0 = time.time()

@@ -4,6 +4,8 @@
 // the data runs in the device kernels of pack.hip, gemv.hip and mfma.hip.
 #include <stdio.h>
 #include <string.h>
+#include <sys/stat.h>
+#include <unistd.h>
 
 #include <map>
 #include <mutex>
@@ -240,6 +242,167 @@ spectra_container* pack_impl(const uint16_t* W_dev, const uint16_t* g_dev, int64
   return c;
 }
 
+// ---- container images on the host (files, import) ----
+
+struct ImageFields {
+  int64_t K, N, K_b, G, n_out;
+  Layout lay;
+};
+
+uint64_t rd64(const unsigned char* p) {
+  uint64_t v;
+  memcpy(&v, p, 8);
+  return v;
+}
+
+// Header checks: fields, shape limits, offsets equal to the layout, total.
+int parse_header(const unsigned char* h, uint64_t bytes, ImageFields& f) {
+  if (bytes < kHeaderBytes) return fail(SPECTRA_E_INVAL, "image shorter than its 128-byte header");
+  const uint64_t w0 = rd64(h);
+  if ((uint32_t)w0 != kMagic) return fail(SPECTRA_E_INVAL, "bad magic");
+  if ((uint32_t)(w0 >> 32) != kVersion) return fail(SPECTRA_E_INVAL, "unsupported version");
+  f.K = (int64_t)rd64(h + 8);
+  f.N = (int64_t)rd64(h + 16);
+  f.K_b = (int64_t)rd64(h + 24);
+  f.G = (int64_t)rd64(h + 32);
+  f.n_out = (int64_t)rd64(h + 40);
+  if (check_shape(f.K, f.N) != SPECTRA_OK) return SPECTRA_E_INVAL;
+  if (f.n_out < 0 || f.n_out > f.K) return fail(SPECTRA_E_INVAL, "n_out out of range [0, K]");
+  if (f.K_b != f.K - f.n_out) return fail(SPECTRA_E_INVAL, "K_b != K - n_out");
+  if (f.G != (f.K_b + kGroup - 1) / kGroup) return fail(SPECTRA_E_INVAL, "G != ceil(K_b / 32)");
+  f.lay = make_layout(f.K, f.N, f.n_out);
+  const uint64_t want[7] = {f.lay.mask, f.lay.perm, f.lay.codes, f.lay.scales,
+                            f.lay.zeros, f.lay.outliers, f.lay.total};
+  for (int i = 0; i < 7; ++i)
+    if (rd64(h + 48 + 8 * i) != want[i]) return fail(SPECTRA_E_INVAL, "section offsets differ from the layout");
+  if (bytes != f.lay.total) return fail(SPECTRA_E_INVAL, "image size differs from total_bytes");
+  return SPECTRA_OK;
+}
+
+// Checks on the bytes [pos, pos + len) of the image (any split into ranges
+// at even positions): scales finite and >= 0, heavy-tailed weights finite,
+// the zero nibble past N*G zero.
+int check_range(const ImageFields& f, uint64_t pos, const unsigned char* p, uint64_t len) {
+  const uint64_t NG = (uint64_t)f.N * (uint64_t)f.G;
+  auto overlap = [&](uint64_t a, uint64_t b, uint64_t& lo, uint64_t& hi) {
+    lo = a > pos ? a : pos;
+    hi = b < pos + len ? b : pos + len;
+    return lo < hi;
+  };
+  uint64_t lo, hi;
+  if (overlap(f.lay.scales, f.lay.scales + 2 * NG, lo, hi)) {
+    for (uint64_t b = lo; b < hi; b += 2) {
+      uint16_t h;
+      memcpy(&h, p + (b - pos), 2);
+      if ((h & 0x8000u) || (h & 0x7C00u) == 0x7C00u)
+        return fail(SPECTRA_E_INVAL, "a scale is negative or not finite");
+    }
+  }
+  const uint64_t ob = 2ull * (uint64_t)f.N * (uint64_t)f.n_out;
+  if (overlap(f.lay.outliers, f.lay.outliers + ob, lo, hi)) {
+    for (uint64_t b = lo; b < hi; b += 2) {
+      uint16_t h;
+      memcpy(&h, p + (b - pos), 2);
+      if ((h & 0x7C00u) == 0x7C00u) return fail(SPECTRA_E_INVAL, "a heavy-tailed weight is not finite");
+    }
+  }
+  if (NG & 1) {
+    const uint64_t last = f.lay.zeros + NG / 2;  // byte holding the final nibble
+    if (last >= pos && last < pos + len && (p[last - pos] >> 4) != 0)
+      return fail(SPECTRA_E_INVAL, "the unused zero nibble is not 0");
+  }
+  return SPECTRA_OK;
+}
+
+// mask: n_out bits set, none past K; perm: bulk channels ascending, then the
+// heavy-tailed ones ascending (the only order the packer writes).
+int check_meta(const ImageFields& f, const uint32_t* mask, const int32_t* perm) {
+  const int64_t words = (f.K + 31) / 32;
+  int64_t set = 0;
+  for (int64_t w = 0; w < words; ++w) {
+    uint32_t m = mask[w];
+    if (w == words - 1 && (f.K & 31)) {
+      if (m >> (f.K & 31)) return fail(SPECTRA_E_INVAL, "mask bits set past K");
+    }
+    set += __builtin_popcount(m);
+  }
+  if (set != f.n_out) return fail(SPECTRA_E_INVAL, "mask does not flag n_out channels");
+  int64_t b = 0, o = f.K_b;
+  for (int64_t k = 0; k < f.K; ++k) {
+    const bool heavy = (mask[k >> 5] >> (k & 31)) & 1u;
+    const int64_t at = heavy ? o++ : b++;
+    if (perm[at] != (int32_t)k) return fail(SPECTRA_E_INVAL, "perm is not the canonical channel order");
+  }
+  return SPECTRA_OK;
+}
+
+int validate_host_image(const unsigned char* img, uint64_t bytes, ImageFields& f) {
+  if (parse_header(img, bytes, f) != SPECTRA_OK) return SPECTRA_E_INVAL;
+  if (check_range(f, 0, img, bytes) != SPECTRA_OK) return SPECTRA_E_INVAL;
+  return check_meta(f, reinterpret_cast<const uint32_t*>(img + f.lay.mask),
+                    reinterpret_cast<const int32_t*>(img + f.lay.perm));
+}
+
+// A registered container for fields f with a fresh device image (contents
+// to be filled by the caller); nullptr with the error set on failure.
+spectra_container* new_container(const ImageFields& f) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error(hip_msg("hipGetDevice", e));
+    return nullptr;
+  }
+  spectra_container* c = new (std::nothrow) spectra_container();
+  if (!c) {
+    set_error("host allocation of the container handle failed");
+    return nullptr;
+  }
+  c->tag = kLiveTag;
+  c->device = dev;
+  c->K = f.K;
+  c->N = f.N;
+  c->K_b = f.K_b;
+  c->G = f.G;
+  c->n_out = f.n_out;
+  c->lay = f.lay;
+  void* p = nullptr;
+  e = hipMalloc(&p, f.lay.total);
+  if (e != hipSuccess) {
+    delete c;
+    set_error(hip_msg("hipMalloc (container)", e));
+    return nullptr;
+  }
+  c->dev = static_cast<unsigned char*>(p);
+  return c;
+}
+
+void drop_container(spectra_container* c) {
+  if (!c) return;
+  if (c->dev) (void)hipFree(c->dev);
+  delete c;
+}
+
+uint64_t chunk_size(uint64_t want) {
+  uint64_t c = want == 0 ? (8ull << 20) : want;
+  if (c < 4096) c = 4096;
+  return (c + 255) / 256 * 256;
+}
+
+// Pinned host staging buffers, freed on scope exit.
+struct Pinned {
+  void* p = nullptr;
+  ~Pinned() {
+    if (p) (void)hipHostFree(p);
+  }
+};
+
+struct File {
+  FILE* fp = nullptr;
+  ~File() {
+    if (fp) fclose(fp);
+  }
+};
+
 }  // namespace
 }  // namespace spectra
 
@@ -396,6 +559,149 @@ int spectra_embed(const spectra_container* c, const void* ids, int64_t T, void* 
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("row gather launch", e));
   return SPECTRA_OK;
+}
+
+int spectra_validate_image(const void* image, uint64_t bytes) {
+  if (!image) return fail(SPECTRA_E_INVAL, "null image");
+  ImageFields f;
+  return validate_host_image(static_cast<const unsigned char*>(image), bytes, f);
+}
+
+spectra_container* spectra_import(const void* image, uint64_t bytes) {
+  if (!image) {
+    set_error("null image");
+    return nullptr;
+  }
+  ImageFields f;
+  if (validate_host_image(static_cast<const unsigned char*>(image), bytes, f) != SPECTRA_OK) return nullptr;
+  spectra_container* c = new_container(f);
+  if (!c) return nullptr;
+  const hipError_t e = hipMemcpy(c->dev, image, bytes, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    drop_container(c);
+    set_error(hip_msg("upload of the image", e));
+    return nullptr;
+  }
+  register_handle(c);
+  return c;
+}
+
+int spectra_save(const spectra_container* c, const char* path, uint64_t chunk_bytes) {
+  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+  if (!path) return fail(SPECTRA_E_INVAL, "null path");
+  const uint64_t chunk = chunk_size(chunk_bytes);
+  Pinned stage;
+  hipError_t e = hipHostMalloc(&stage.p, chunk, hipHostMallocDefault);
+  if (e != hipSuccess) return fail(SPECTRA_E_NOMEM, hip_msg("pinned staging buffer", e));
+  int st = SPECTRA_OK;
+  {
+    File out;
+    out.fp = fopen(path, "wb");
+    if (!out.fp) return fail(SPECTRA_E_IO, std::string("cannot create ") + path);
+    for (uint64_t pos = 0; pos < c->lay.total && st == SPECTRA_OK; pos += chunk) {
+      const uint64_t n = c->lay.total - pos < chunk ? c->lay.total - pos : chunk;
+      e = hipMemcpy(stage.p, c->dev + pos, n, hipMemcpyDeviceToHost);
+      if (e != hipSuccess) st = fail(SPECTRA_E_HIP, hip_msg("copy of the image", e));
+      else if (fwrite(stage.p, 1, n, out.fp) != n) st = fail(SPECTRA_E_IO, std::string("write to ") + path + " failed");
+    }
+    if (st == SPECTRA_OK && fflush(out.fp) != 0) st = fail(SPECTRA_E_IO, std::string("write to ") + path + " failed");
+    if (fclose(out.fp) != 0 && st == SPECTRA_OK) st = fail(SPECTRA_E_IO, std::string("close of ") + path + " failed");
+    out.fp = nullptr;
+  }
+  if (st != SPECTRA_OK) (void)unlink(path);
+  return st;
+}
+
+spectra_container* spectra_load(const char* path, uint64_t chunk_bytes) {
+  if (!path) {
+    set_error("null path");
+    return nullptr;
+  }
+  File in;
+  in.fp = fopen(path, "rb");
+  if (!in.fp) {
+    set_error(std::string("cannot open ") + path);
+    return nullptr;
+  }
+  struct stat sb;
+  if (fstat(fileno(in.fp), &sb) != 0 || sb.st_size < 0) {
+    set_error(std::string("cannot stat ") + path);
+    return nullptr;
+  }
+  const uint64_t bytes = (uint64_t)sb.st_size;
+  unsigned char hdr[kHeaderBytes];
+  if (bytes < kHeaderBytes || fread(hdr, 1, kHeaderBytes, in.fp) != kHeaderBytes) {
+    set_error(std::string(path) + ": shorter than a container header");
+    return nullptr;
+  }
+  ImageFields f;
+  if (parse_header(hdr, bytes, f) != SPECTRA_OK) return nullptr;
+  if (fseek(in.fp, 0, SEEK_SET) != 0) {
+    set_error(std::string("cannot rewind ") + path);
+    return nullptr;
+  }
+  const uint64_t chunk = chunk_size(chunk_bytes);
+  Pinned stage[2];
+  for (int i = 0; i < 2; ++i) {
+    const hipError_t e = hipHostMalloc(&stage[i].p, chunk, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      set_error(hip_msg("pinned staging buffer", e));
+      return nullptr;
+    }
+  }
+  hipStream_t s = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+    set_error("stream creation failed");
+    return nullptr;
+  }
+  hipEvent_t done[2] = {nullptr, nullptr};
+  for (int i = 0; i < 2; ++i) (void)hipEventCreateWithFlags(&done[i], hipEventDisableTiming);
+  spectra_container* c = new_container(f);
+  // mask and perm are kept on the host as they pass, for the final check
+  std::vector<unsigned char> meta(f.lay.codes - f.lay.mask);
+  int st = c ? SPECTRA_OK : SPECTRA_E_NOMEM;
+  bool used[2] = {false, false};
+  for (uint64_t pos = 0, k = 0; st == SPECTRA_OK && pos < bytes; pos += chunk, ++k) {
+    const int b = (int)(k & 1);
+    const uint64_t n = bytes - pos < chunk ? bytes - pos : chunk;
+    // the buffer's previous upload must be done before it is refilled
+    if (used[b] && hipEventSynchronize(done[b]) != hipSuccess) {
+      st = fail(SPECTRA_E_HIP, "staging upload failed");
+      break;
+    }
+    unsigned char* buf = static_cast<unsigned char*>(stage[b].p);
+    if (fread(buf, 1, n, in.fp) != n) {
+      st = fail(SPECTRA_E_IO, std::string("read of ") + path + " failed");
+      break;
+    }
+    if (check_range(f, pos, buf, n) != SPECTRA_OK) {
+      st = SPECTRA_E_INVAL;
+      break;
+    }
+    const uint64_t mlo = pos > f.lay.mask ? pos : f.lay.mask;
+    const uint64_t mhi = pos + n < f.lay.codes ? pos + n : f.lay.codes;
+    if (mlo < mhi) memcpy(meta.data() + (mlo - f.lay.mask), buf + (mlo - pos), mhi - mlo);
+    hipError_t e = hipMemcpyAsync(c->dev + pos, buf, n, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipEventRecord(done[b], s);
+    if (e != hipSuccess) {
+      st = fail(SPECTRA_E_HIP, hip_msg("upload of the image", e));
+      break;
+    }
+    used[b] = true;
+  }
+  if (hipStreamSynchronize(s) != hipSuccess && st == SPECTRA_OK) st = fail(SPECTRA_E_HIP, "upload failed");
+  if (st == SPECTRA_OK)
+    st = check_meta(f, reinterpret_cast<const uint32_t*>(meta.data()),
+                    reinterpret_cast<const int32_t*>(meta.data() + (f.lay.perm - f.lay.mask)));
+  for (int i = 0; i < 2; ++i)
+    if (done[i]) (void)hipEventDestroy(done[i]);
+  (void)hipStreamDestroy(s);
+  if (st != SPECTRA_OK) {
+    drop_container(c);
+    return nullptr;
+  }
+  register_handle(c);
+  return c;
 }
 
 }  // extern "C"

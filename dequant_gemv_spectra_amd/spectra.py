@@ -20,12 +20,14 @@ SPECTRA_E_NONFINITE = -2
 SPECTRA_E_NOMEM = -3
 SPECTRA_E_HIP = -4
 SPECTRA_E_UNSUPPORTED = -5
+SPECTRA_E_IO = -6
 
 KERNELS = {"auto": 0, "gemv": 1, "mfma": 2}
 
 EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm_ex",
             "spectra_gemm_grouped", "spectra_embed", "spectra_free", "spectra_info",
-            "spectra_export", "spectra_last_error", "spectra_version"]
+            "spectra_export", "spectra_validate_image", "spectra_import", "spectra_save",
+            "spectra_load", "spectra_last_error", "spectra_version"]
 
 
 class SpectraError(RuntimeError):
@@ -68,6 +70,14 @@ def lib() -> ctypes.CDLL:
     L.spectra_gemm_grouped.restype = c_int
     L.spectra_embed.argtypes = [vp, vp, i64, vp, vp]
     L.spectra_embed.restype = c_int
+    L.spectra_validate_image.argtypes = [vp, u64]
+    L.spectra_validate_image.restype = c_int
+    L.spectra_import.argtypes = [vp, u64]
+    L.spectra_import.restype = vp
+    L.spectra_save.argtypes = [vp, ctypes.c_char_p, u64]
+    L.spectra_save.restype = c_int
+    L.spectra_load.argtypes = [ctypes.c_char_p, u64]
+    L.spectra_load.restype = vp
     L.spectra_free.argtypes = [vp]
     L.spectra_free.restype = None
     L.spectra_info.argtypes = [vp, ctypes.POINTER(spectra_info_t)]
@@ -212,6 +222,43 @@ def spectra_embed(c: Container, ids, out=None, stream=None):
     _check(lib().spectra_embed(c.handle, ctypes.c_void_p(ids.data_ptr()), T,
                                ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
     return out
+
+
+def _status_of(msg: str) -> int:
+    if msg.startswith("cannot ") or "read of" in msg or "write to" in msg:
+        return SPECTRA_E_IO
+    if "hipMalloc" in msg or "pinned" in msg:
+        return SPECTRA_E_NOMEM
+    return SPECTRA_E_INVAL
+
+
+def spectra_validate_image(image: bytes) -> None:
+    """Raise SpectraError unless `image` is a well-formed container image."""
+    buf = (ctypes.c_ubyte * len(image)).from_buffer_copy(image) if image else None
+    _check(lib().spectra_validate_image(buf, len(image)))
+
+
+def spectra_import(image: bytes) -> Container:
+    """A new container on the current device from a host image."""
+    buf = (ctypes.c_ubyte * len(image)).from_buffer_copy(image) if image else None
+    p = lib().spectra_import(buf, len(image))
+    if not p:
+        msg = spectra_last_error()
+        raise SpectraError(_status_of(msg), msg)
+    return Container(p)
+
+
+def spectra_save(c: Container, path: str, chunk_bytes: int = 0) -> None:
+    _check(lib().spectra_save(c.handle, os.fsencode(path), chunk_bytes))
+
+
+def spectra_load(path: str, chunk_bytes: int = 0) -> Container:
+    """Stream a container file into a new container on the current device."""
+    p = lib().spectra_load(os.fsencode(path), chunk_bytes)
+    if not p:
+        msg = spectra_last_error()
+        raise SpectraError(_status_of(msg), msg)
+    return Container(p)
 
 
 def spectra_free(c: Container):

@@ -113,7 +113,8 @@ typedef enum {
   SPECTRA_E_NONFINITE = -2,    /* W or gamma holds an infinity or a NaN */
   SPECTRA_E_NOMEM = -3,        /* a device or host allocation failed */
   SPECTRA_E_HIP = -4,          /* a HIP runtime call failed (message has the HIP error string) */
-  SPECTRA_E_UNSUPPORTED = -5   /* the forced kernel cannot run this shape */
+  SPECTRA_E_UNSUPPORTED = -5,  /* the forced kernel cannot run this shape */
+  SPECTRA_E_IO = -6            /* a file could not be opened, read or written */
 } spectra_status;
 
 /* Kernel selection for spectra_gemm_ex. */
@@ -206,6 +207,44 @@ int spectra_info(const spectra_container* c, spectra_info_t* out);
 /* Copy the container image (header + sections, total_bytes) to HOST memory
  * host_dst of capacity cap bytes.  E_INVAL if cap < total_bytes.  Synchronous. */
 int spectra_export(const spectra_container* c, void* host_dst, uint64_t cap);
+
+/* ---------------------------------------------------------------------------
+ * Container files.  The SPECTRA page (abstract) serializes every weight,
+ * scale and offset into one self-contained binary container that is streamed
+ * straight into GPU memory so that initialization has a bounded memory spike.
+ * Here the file is the container image itself (layout above, total_bytes
+ * long), and loading streams it through a fixed-size staging buffer: peak
+ * host memory is 2 * chunk_bytes of pinned staging plus the mask and perm
+ * sections (about 4.1 * K bytes), whatever the payload's size.
+ * chunk_bytes = 0 selects 8 MiB; other values are rounded up to a multiple
+ * of 256 and to at least 4096.
+ * ------------------------------------------------------------------------- */
+
+/* Check a container image held in HOST memory without touching any device:
+ * magic and version, K, N, K_b = K - n_out, G = ceil(K_b / 32), section
+ * offsets equal to the layout above, bytes == total_bytes, mask bits past K
+ * zero and n_out of them set, perm = the bulk channels ascending then the
+ * heavy-tailed ones ascending, every scale a finite fp16 >= 0, every
+ * heavy-tailed weight finite, the unused zero nibble 0.  SPECTRA_OK or
+ * SPECTRA_E_INVAL with the first violation in spectra_last_error(). */
+int spectra_validate_image(const void* image, uint64_t bytes);
+
+/* A new container on the current device from a HOST image (validated as
+ * above, then copied).  Synchronous; NULL on error (spectra_last_error). */
+spectra_container* spectra_import(const void* image, uint64_t bytes);
+
+/* Write the container's image to `path` (created or truncated), copying it
+ * out through the staging buffer chunk by chunk.  Synchronous.  E_IO on any
+ * file error (a partial file is removed), E_HIP on a copy error. */
+int spectra_save(const spectra_container* c, const char* path, uint64_t chunk_bytes);
+
+/* Read a container file into a new container on the current device: the
+ * header is checked first, then the file is streamed in chunks (the next
+ * chunk is read from the file while the previous one is copied to the
+ * device) and each chunk is validated as it passes; the mask and perm are
+ * checked once complete.  Synchronous; NULL on error (E_IO, E_INVAL for a
+ * malformed image, E_NOMEM, E_HIP; see spectra_last_error). */
+spectra_container* spectra_load(const char* path, uint64_t chunk_bytes);
 
 /* Thread-local description of the latest error on the calling thread ("" if none). */
 const char* spectra_last_error(void);
