@@ -42,8 +42,11 @@ Parity status of each function (what pins it, in tests/test_oracle_pins.py):
   tolerance          definition written in the header; no independent pin
                      beyond its use (parity unpinned as a formula)
   embed_ref          grid-valued tables gather back bit-exact (bulk and
-                     heavy-tailed channels), pure-Python brute force over the
-                     unpacked fields, out-of-range ids give zero rows
+                     heavy-tailed channels), out-of-range ids give zero rows
+  kv_quantize        grid-valued head vectors round-trip exactly; the same
+                     groups through quantize_groups directly
+  kv_attend_ref      pure-Python brute force (math.exp, explicit sums) on tiny
+                     caches; one-token cache returns V; equal keys average V
 """
 from __future__ import annotations
 
@@ -371,3 +374,76 @@ def embed_ref(img: bytes, ids) -> np.ndarray:
     if ok.any():
         out[ok] = reconstruct_rows(img, ids[ok]).astype(np.float16)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Step 7: the Group-32 4-bit KV cache (quantize on append, attend)
+# ---------------------------------------------------------------------------
+def kv_quantize(x16: np.ndarray):
+    """Quantize key or value vectors on append.
+
+    SPECTRA page ("SPECTRA: Sparse-Precision Exact Channel Tensor
+    Reconstruction Architecture", abstract): the key-value cache is kept in
+    microscaled Group-32 4-bit form.  Reading: each head's vector of D = 32G
+    channels is split into G groups of 32 consecutive channels and quantized
+    exactly as a bulk weight group (same range, scale, zero point and codes;
+    no heavy-tailed split, which the page states for weights only).
+    x16: fp16 [T][H][D].  Returns (q uint8 [T][H][G][32], z uint8 [T][H][G],
+    s16 float16 [T][H][G]).
+    """
+    x = np.asarray(x16, dtype=np.float16)
+    T, H, D = x.shape
+    if D % GROUP:
+        raise ValueError("head dimension must be a multiple of 32")
+    q, z, s16 = quantize_groups(x.reshape(T * H, D).astype(np.float64))
+    G = D // GROUP
+    return q.reshape(T, H, G, GROUP), z.reshape(T, H, G), s16.reshape(T, H, G)
+
+
+def kv_dequantize(q, z, s16) -> np.ndarray:
+    """(q - z) * s16 in binary64: float64 [T][H][D]."""
+    q = np.asarray(q)
+    T, H, G, _ = q.shape
+    w = dequantize_groups(q.reshape(T * H, G, GROUP), np.asarray(z).reshape(T * H, G),
+                          np.asarray(s16).reshape(T * H, G), G * GROUP)
+    return w.reshape(T, H, G * GROUP)
+
+
+def kv_attend_ref(q16: np.ndarray, K_hat: np.ndarray, V_hat: np.ndarray) -> np.ndarray:
+    """Decode-step attention over the dequantized cache, in binary64.
+
+    q16: fp16 [Hq][D] (one query per head); K_hat, V_hat: float64 [L][Hkv][D]
+    with Hq a multiple of Hkv (query head h reads cache head h // (Hq/Hkv)).
+    out[h] = softmax(q_h K_hat^T / sqrt(D)) V_hat, the plain definition
+    (max subtracted before exp only to keep exp finite).
+    """
+    q = np.asarray(q16, dtype=np.float16).astype(np.float64)
+    Hq, D = q.shape
+    L, Hkv, _ = K_hat.shape
+    rep = Hq // Hkv
+    out = np.empty((Hq, D), dtype=np.float64)
+    for h in range(Hq):
+        kv = h // rep
+        s = K_hat[:, kv, :] @ q[h] / np.sqrt(D)
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        out[h] = p @ V_hat[:, kv, :]
+    return out
+
+
+def kv_attend_tolerance(q16: np.ndarray, K_hat: np.ndarray, V_hat: np.ndarray) -> np.ndarray:
+    """Per-element bound 1e-3 * (sum_t p_t |V_hat[t]|)[h][d] + 1e-6: the GEMM
+    bound with the weights read as V_hat and the input as the softmax
+    weights (fp16 output rounding spends 2^-11 of it)."""
+    q = np.asarray(q16, dtype=np.float16).astype(np.float64)
+    Hq, D = q.shape
+    L, Hkv, _ = K_hat.shape
+    rep = Hq // Hkv
+    t = np.empty((Hq, D), dtype=np.float64)
+    for h in range(Hq):
+        kv = h // rep
+        s = K_hat[:, kv, :] @ q[h] / np.sqrt(D)
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        t[h] = p @ np.abs(V_hat[:, kv, :])
+    return 1e-3 * t + 1e-6

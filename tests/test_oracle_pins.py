@@ -388,3 +388,70 @@ def test_embed_ref_out_of_range_rows_are_zero_and_match_unpack():
         else:
             assert not out[i].any()
     assert O.embed_ref(img, np.zeros(0, np.int64)).shape == (0, 70)
+
+
+# --------------------------------------------------------------------------
+# Group-32 4-bit KV cache
+# --------------------------------------------------------------------------
+def test_kv_quantize_grid_vectors_round_trip():
+    rng = np.random.default_rng(21)
+    T, H, D, e = 5, 3, 128, -7
+    x = np.zeros((T, H, D))
+    for t in range(T):
+        for h in range(H):
+            for g in range(D // 32):
+                z = int(rng.integers(0, 16))
+                q = rng.integers(0, 16, 32)
+                q[rng.choice(32, 2, replace=False)] = [0, 15]
+                x[t, h, 32 * g:32 * g + 32] = (q - z) * 2.0 ** e
+    x16 = x.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), x)
+    q, z, s16 = O.kv_quantize(x16)
+    assert np.all(s16.astype(np.float64) == 2.0 ** e)
+    assert np.array_equal(O.kv_dequantize(q, z, s16), x)
+
+
+def test_kv_quantize_is_the_weight_quantizer_per_head():
+    x16 = (np.random.default_rng(22).standard_normal((4, 2, 64))).astype(np.float16)
+    q, z, s16 = O.kv_quantize(x16)
+    q2, z2, s2 = O.quantize_groups(x16.reshape(8, 64).astype(np.float64))
+    assert np.array_equal(q.reshape(8, 2, 32), q2) and np.array_equal(z.reshape(8, 2), z2)
+    assert np.array_equal(s16.reshape(8, 2), s2)
+
+
+def _attend_brute(q, K, V):
+    import math
+    Hq, D = len(q), len(q[0])
+    L, Hkv = len(K), len(K[0])
+    rep = Hq // Hkv
+    out = []
+    for h in range(Hq):
+        kv = h // rep
+        s = [sum(float(q[h][d]) * K[t][kv][d] for d in range(D)) / math.sqrt(D) for t in range(L)]
+        m = max(s)
+        w = [math.exp(v - m) for v in s]
+        tot = sum(w)
+        out.append([sum(w[t] * V[t][kv][d] for t in range(L)) / tot for d in range(D)])
+    return out
+
+
+@pytest.mark.parametrize("L,Hkv,rep,D,seed", [(1, 1, 1, 32, 0), (7, 2, 2, 32, 1), (13, 1, 4, 64, 2)])
+def test_kv_attend_ref_brute_force(L, Hkv, rep, D, seed):
+    rng = np.random.default_rng(seed)
+    q16 = rng.standard_normal((Hkv * rep, D)).astype(np.float16)
+    K = rng.standard_normal((L, Hkv, D))
+    V = rng.standard_normal((L, Hkv, D))
+    ref = O.kv_attend_ref(q16, K, V)
+    brute = np.array(_attend_brute(q16.astype(np.float64).tolist(), K.tolist(), V.tolist()))
+    np.testing.assert_allclose(ref, brute, rtol=1e-12, atol=1e-14)
+    if L == 1:
+        assert np.allclose(ref, np.repeat(V[0], rep, axis=0))
+
+
+def test_kv_attend_equal_keys_average_values():
+    rng = np.random.default_rng(23)
+    L, D = 9, 32
+    K = np.tile(rng.standard_normal((1, 1, D)), (L, 1, 1))
+    V = rng.standard_normal((L, 1, D))
+    q16 = rng.standard_normal((1, D)).astype(np.float16)
+    np.testing.assert_allclose(O.kv_attend_ref(q16, K, V)[0], V[:, 0, :].mean(axis=0), rtol=1e-13)
