@@ -21,7 +21,8 @@ serve the weights; cfg2 stacks the 1.5B-class layer 28 deep.  `embed` times
 the fused embedding gather instead (its own metric): --tokens random rows of
 the 131072 x 3072 table per step, rotated over copies the same way; bytes =
 the gathered rows' payload + the fp16 rows written + the ids.  `load` times
-spectra_load of the 241 MB container file through the chunked staging path.
+spectra_load of the 241 MB container file through the chunked staging path;
+`kv` times decode attention over the Group-32 4-bit KV cache.
 
 Prints ONE JSON line.  roofline: the dominant kernel (largest share of step
 bytes) is replayed alone as a captured graph and timed with HIP events on its
@@ -50,9 +51,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="cfg3", choices=["cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "embed", "load"])
+    ap.add_argument("--workload", default="cfg3", choices=["cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "embed", "load", "kv"])
     ap.add_argument("--tokens", type=int, default=16384, help="embed: token ids gathered per step")
     ap.add_argument("--chunk-mib", type=int, default=8, help="load: staging chunk size")
+    ap.add_argument("--context", type=int, default=8192, help="kv: cached tokens attended per step")
     ap.add_argument("--M", type=int, default=1)
     ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "mfma"])
     ap.add_argument("--layers", type=int, default=None, help="cfg3: fewer layers (quick runs)")
@@ -267,6 +269,56 @@ def run_load(args, sp, torch):
     print(json.dumps(out), flush=True)
 
 
+KV_METRIC = "G32 4-bit KV-cache decode attention: effective HBM GB/s (quantized K and V read)"
+
+
+def run_kv(args, sp, torch):
+    """One step = decode attention of 32 query heads over 8 cache heads of 128
+    channels (the 4B-class layer) with --context cached tokens, rotating over
+    distinct caches (>= 1 GiB) so they stream from HBM."""
+    import numpy as np
+    H, rep_, D, L = 8, 4, 128, args.context
+    per = 2 * L * H * (D // 32) * (16 + 2) + L * H * (D // 32)  # K and V records, scales, zero bytes
+    copies = max(1, int(args.rotate_gib * 2 ** 30 // per) + 1)
+    rng = np.random.default_rng(31)
+    caches = []
+    for i in range(copies):
+        kv = sp.KvCache(L, H, D)
+        k = torch.from_numpy(rng.standard_normal((L, H, D)).astype(np.float16)).cuda()
+        v = torch.from_numpy((rng.standard_normal((L, H, D)) * 0.5).astype(np.float16)).cuda()
+        kv.append(k, v)
+        caches.append(kv)
+    q = torch.from_numpy(rng.standard_normal((H * rep_, D)).astype(np.float16)).cuda()
+    outs = [torch.empty_like(q) for _ in caches]
+    step_bytes = per + 2 * 2 * H * rep_ * D
+    log(f"kv: {copies} caches of {L} tokens, {per / 1e6:.2f} MB each")
+
+    def mk(kv, o):
+        def f():
+            kv.attend(q, out=o)
+        return f
+    fns = [mk(kv, o) for kv, o in zip(caches, outs)]
+    graph = capture(torch, fns)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // len(fns))
+    ms = time_graph(torch, graph, reps) / len(fns)
+    value = step_bytes / (ms * 1e-3) / 1e9
+    out = {"metric": KV_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+           "data": "synthetic",
+           "config": {"workload": f"kv-attend-{H * rep_}q-{H}kv-{D}d-{L}ctx", "bytes_per_step": int(step_bytes),
+                      "launches_per_step": 3, "hip_graph": True, "parallelism": "single GPU"},
+           "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
+                        "kernel": "k_kv_scores + k_kv_pv + k_kv_combine", "avg_launch_us": round(ms * 1e3, 3),
+                        "bytes_per_launch": int(step_bytes)},
+           "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
 _CAPTURE_STREAM = None
 
 
@@ -356,6 +408,9 @@ def main():
         return
     if args.workload == "load":
         run_load(args, sp, torch)
+        return
+    if args.workload == "kv":
+        run_kv(args, sp, torch)
         return
     cfg = int(args.workload[3:])
     t0 = time.time()

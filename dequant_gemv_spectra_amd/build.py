@@ -27,6 +27,7 @@ SOURCES = {
     "gemv.hip": [],
     "mfma.hip": [],
     "embed.hip": [],
+    "kv.hip": ["-ffp-contract=off"],
 }
 
 COMMON = [

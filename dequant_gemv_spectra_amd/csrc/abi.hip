@@ -403,6 +403,36 @@ struct File {
   }
 };
 
+// ---- KV caches ----
+
+struct KvRegistry {
+  std::mutex mu;
+  std::unordered_set<const spectra_kv*> live;
+};
+KvRegistry& kv_registry() {
+  static KvRegistry r;
+  return r;
+}
+
+}  // namespace
+}  // namespace spectra
+
+struct spectra_kv {
+  int device;
+  int64_t length;
+  spectra::KvView view;
+  unsigned char* dev;  // one allocation: K records, scales, zeros, then V's
+  uint64_t plane_bytes[3];  // per plane: records, scales, zeros (capacity-sized)
+};
+
+namespace spectra {
+namespace {
+bool kv_live(const spectra_kv* kv) {
+  if (!kv) return false;
+  KvRegistry& r = kv_registry();
+  std::lock_guard<std::mutex> lk(r.mu);
+  return r.live.count(kv) != 0;
+}
 }  // namespace
 }  // namespace spectra
 
@@ -702,6 +732,136 @@ spectra_container* spectra_load(const char* path, uint64_t chunk_bytes) {
   }
   register_handle(c);
   return c;
+}
+
+spectra_kv* spectra_kv_create(int64_t capacity, int32_t heads, int32_t head_dim) {
+  if (capacity < 1 || capacity > ((int64_t)1 << 31) || !kv_shape_supported(heads, head_dim)) {
+    set_error("KV cache: capacity in [1, 2^31], heads in [1, 1024], head_dim 64, 128 or 256");
+    return nullptr;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error(hip_msg("hipGetDevice", e));
+    return nullptr;
+  }
+  const uint64_t G = (uint64_t)head_dim / 32;
+  const uint64_t n = (uint64_t)capacity * (uint64_t)heads * G;  // groups per plane
+  const uint64_t rec = align_up(16 * n), sc = align_up(2 * n), zb = align_up(n / 2);
+  spectra_kv* kv = new (std::nothrow) spectra_kv();
+  if (!kv) {
+    set_error("host allocation of the KV handle failed");
+    return nullptr;
+  }
+  void* p = nullptr;
+  e = hipMalloc(&p, 2 * (rec + sc + zb));
+  if (e != hipSuccess) {
+    delete kv;
+    set_error(hip_msg("hipMalloc (KV cache)", e));
+    return nullptr;
+  }
+  unsigned char* b = static_cast<unsigned char*>(p);
+  kv->device = dev;
+  kv->length = 0;
+  kv->dev = b;
+  kv->plane_bytes[0] = rec;
+  kv->plane_bytes[1] = sc;
+  kv->plane_bytes[2] = zb;
+  KvView& v = kv->view;
+  v.k.codes = reinterpret_cast<uint4*>(b);
+  v.k.scales = reinterpret_cast<uint16_t*>(b + rec);
+  v.k.zeros = b + rec + sc;
+  unsigned char* b2 = b + rec + sc + zb;
+  v.v.codes = reinterpret_cast<uint4*>(b2);
+  v.v.scales = reinterpret_cast<uint16_t*>(b2 + rec);
+  v.v.zeros = b2 + rec + sc;
+  v.cap = capacity;
+  v.H = heads;
+  v.D = head_dim;
+  v.G = (int32_t)G;
+  KvRegistry& r = kv_registry();
+  std::lock_guard<std::mutex> lk(r.mu);
+  r.live.insert(kv);
+  return kv;
+}
+
+int spectra_kv_append(spectra_kv* kv, const void* k, const void* v, int64_t T, void* stream) {
+  if (!kv_live(kv)) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
+  if (T < 0) return fail(SPECTRA_E_INVAL, "T < 0");
+  if (T > kv->view.cap - kv->length) return fail(SPECTRA_E_INVAL, "append past the KV cache capacity");
+  if (T == 0) return SPECTRA_OK;
+  if (!k || !v) return fail(SPECTRA_E_INVAL, "null k or v");
+  if ((reinterpret_cast<uintptr_t>(k) & 15) || (reinterpret_cast<uintptr_t>(v) & 15))
+    return fail(SPECTRA_E_INVAL, "k and v must be 16-byte aligned");
+  const hipError_t e = launch_kv_append(kv->view, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                        T, kv->length, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("KV append launch", e));
+  kv->length += T;
+  return SPECTRA_OK;
+}
+
+int spectra_kv_attend(const spectra_kv* kv, const void* q, int32_t q_heads, void* out, void* stream) {
+  if (!kv_live(kv)) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
+  if (kv->length < 1) return fail(SPECTRA_E_INVAL, "attention over an empty KV cache");
+  if (kv->length > kv_max_attend_length())
+    return fail(SPECTRA_E_UNSUPPORTED, "attention over more than 524288 cached tokens");
+  if (!q || !out) return fail(SPECTRA_E_INVAL, "null q or out");
+  if ((reinterpret_cast<uintptr_t>(q) & 3) || (reinterpret_cast<uintptr_t>(out) & 3))
+    return fail(SPECTRA_E_INVAL, "q and out must be 4-byte aligned");
+  const int H = kv->view.H;
+  if (q_heads < H || q_heads % H != 0 || q_heads / H > kv_max_rep())
+    return fail(SPECTRA_E_INVAL, "q_heads must be heads times 1 .. 16");
+  const int rep = q_heads / H;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  hipError_t e = stream_workspace(kv->device, s, kv_attend_workspace_bytes(kv->view, rep, kv->length), &ws);
+  if (e != hipSuccess) return fail(SPECTRA_E_NOMEM, hip_msg("KV attention workspace", e));
+  e = launch_kv_attend(kv->view, static_cast<const uint16_t*>(q), rep, kv->length, static_cast<uint16_t*>(out),
+                       ws, s);
+  if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("KV attention launch", e));
+  return SPECTRA_OK;
+}
+
+int64_t spectra_kv_length(const spectra_kv* kv) { return kv_live(kv) ? kv->length : -1; }
+
+int spectra_kv_reset(spectra_kv* kv) {
+  if (!kv_live(kv)) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
+  kv->length = 0;
+  return SPECTRA_OK;
+}
+
+int spectra_kv_export(const spectra_kv* kv, void* host_dst, uint64_t cap) {
+  if (!kv_live(kv)) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
+  if (!host_dst) return fail(SPECTRA_E_INVAL, "null destination");
+  const uint64_t n = (uint64_t)kv->length * (uint64_t)kv->view.H * (uint64_t)kv->view.G;
+  const uint64_t part[3] = {16 * n, 2 * n, n / 2};
+  if (cap < 2 * (part[0] + part[1] + part[2])) return fail(SPECTRA_E_INVAL, "destination too small");
+  unsigned char* dst = static_cast<unsigned char*>(host_dst);
+  const unsigned char* planes[2] = {kv->dev, kv->dev + kv->plane_bytes[0] + kv->plane_bytes[1] + kv->plane_bytes[2]};
+  for (int pl = 0; pl < 2; ++pl) {
+    uint64_t off = 0;
+    for (int i = 0; i < 3; ++i) {
+      const hipError_t e = hipMemcpy(dst, planes[pl] + off, part[i], hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("KV export copy", e));
+      dst += part[i];
+      off += kv->plane_bytes[i];
+    }
+  }
+  return SPECTRA_OK;
+}
+
+void spectra_kv_free(spectra_kv* kv) {
+  {
+    KvRegistry& r = kv_registry();
+    std::lock_guard<std::mutex> lk(r.mu);
+    if (!kv || r.live.erase(kv) == 0) return;
+  }
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  if (cur != kv->device) (void)hipSetDevice(kv->device);
+  (void)hipFree(kv->dev);
+  if (cur >= 0 && cur != kv->device) (void)hipSetDevice(cur);
+  delete kv;
 }
 
 }  // extern "C"

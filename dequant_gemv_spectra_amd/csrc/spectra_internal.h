@@ -121,6 +121,26 @@ bool embed_supports(const DeviceView& v);
 hipError_t launch_embed(const DeviceView& v, const int32_t* ids, int64_t T, uint16_t* out,
                         hipStream_t s);
 
+// ---- Group-32 4-bit KV cache (kv.hip) ----
+struct KvPlane {
+  uint4* codes;     // [cap][H][G] 16-byte records
+  uint16_t* scales; // [cap][H][G] fp16 bits
+  uint8_t* zeros;   // [cap][H][G/2] nibbles
+};
+struct KvView {
+  KvPlane k, v;
+  int64_t cap;
+  int32_t H, D, G;
+};
+bool kv_shape_supported(int64_t heads, int64_t head_dim);
+int kv_max_rep();
+int64_t kv_max_attend_length();  // cached tokens one attention call handles
+size_t kv_attend_workspace_bytes(const KvView& c, int rep, int64_t L);
+hipError_t launch_kv_append(const KvView& c, const uint16_t* k, const uint16_t* v, int64_t T, int64_t pos0,
+                            hipStream_t s);
+hipError_t launch_kv_attend(const KvView& c, const uint16_t* q, int rep, int64_t L, uint16_t* out, void* ws,
+                            hipStream_t s);
+
 // ---- per-stream workspace (abi.hip) ----
 // A device buffer of at least `bytes` reserved for work enqueued on stream s
 // of `device`; grown on demand (growth waits for s and reallocates).

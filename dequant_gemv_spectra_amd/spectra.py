@@ -27,7 +27,9 @@ KERNELS = {"auto": 0, "gemv": 1, "mfma": 2}
 EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm_ex",
             "spectra_gemm_grouped", "spectra_embed", "spectra_free", "spectra_info",
             "spectra_export", "spectra_validate_image", "spectra_import", "spectra_save",
-            "spectra_load", "spectra_last_error", "spectra_version"]
+            "spectra_load", "spectra_kv_create", "spectra_kv_append", "spectra_kv_attend",
+            "spectra_kv_length", "spectra_kv_reset", "spectra_kv_export", "spectra_kv_free",
+            "spectra_last_error", "spectra_version"]
 
 
 class SpectraError(RuntimeError):
@@ -78,6 +80,20 @@ def lib() -> ctypes.CDLL:
     L.spectra_save.restype = c_int
     L.spectra_load.argtypes = [ctypes.c_char_p, u64]
     L.spectra_load.restype = vp
+    L.spectra_kv_create.argtypes = [i64, ctypes.c_int32, ctypes.c_int32]
+    L.spectra_kv_create.restype = vp
+    L.spectra_kv_append.argtypes = [vp, vp, vp, i64, vp]
+    L.spectra_kv_append.restype = c_int
+    L.spectra_kv_attend.argtypes = [vp, vp, ctypes.c_int32, vp, vp]
+    L.spectra_kv_attend.restype = c_int
+    L.spectra_kv_length.argtypes = [vp]
+    L.spectra_kv_length.restype = i64
+    L.spectra_kv_reset.argtypes = [vp]
+    L.spectra_kv_reset.restype = c_int
+    L.spectra_kv_export.argtypes = [vp, vp, u64]
+    L.spectra_kv_export.restype = c_int
+    L.spectra_kv_free.argtypes = [vp]
+    L.spectra_kv_free.restype = None
     L.spectra_free.argtypes = [vp]
     L.spectra_free.restype = None
     L.spectra_info.argtypes = [vp, ctypes.POINTER(spectra_info_t)]
@@ -259,6 +275,64 @@ def spectra_load(path: str, chunk_bytes: int = 0) -> Container:
         msg = spectra_last_error()
         raise SpectraError(_status_of(msg), msg)
     return Container(p)
+
+
+class KvCache:
+    """Owning handle of a Group-32 4-bit KV cache (one attention layer)."""
+
+    def __init__(self, capacity: int, heads: int, head_dim: int):
+        p = lib().spectra_kv_create(capacity, heads, head_dim)
+        if not p:
+            raise SpectraError(SPECTRA_E_INVAL, spectra_last_error())
+        self.handle = ctypes.c_void_p(p)
+        self.heads, self.head_dim = heads, head_dim
+
+    def append(self, k, v, stream=None) -> None:
+        """k, v: CUDA fp16 [T][heads][head_dim]."""
+        import torch
+        for t in (k, v):
+            if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 3 or tuple(t.shape[1:]) != (self.heads, self.head_dim):
+                raise ValueError("k and v must be CUDA float16 tensors of shape [T][heads][head_dim]")
+        k, v = k.contiguous(), v.contiguous()
+        _check(lib().spectra_kv_append(self.handle, ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                       k.shape[0], _stream_ptr(stream)))
+
+    def attend(self, q, out=None, stream=None):
+        """q: CUDA fp16 [q_heads][head_dim] -> out fp16 [q_heads][head_dim]."""
+        import torch
+        if q.dtype != torch.float16 or not q.is_cuda or q.dim() != 2 or q.shape[1] != self.head_dim:
+            raise ValueError("q must be a CUDA float16 tensor of shape [q_heads][head_dim]")
+        q = q.contiguous()
+        if out is None:
+            out = torch.empty_like(q)
+        _check(lib().spectra_kv_attend(self.handle, ctypes.c_void_p(q.data_ptr()), q.shape[0],
+                                       ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+        return out
+
+    @property
+    def length(self) -> int:
+        return int(lib().spectra_kv_length(self.handle))
+
+    def reset(self) -> None:
+        _check(lib().spectra_kv_reset(self.handle))
+
+    def export(self) -> bytes:
+        n = self.length * self.heads * (self.head_dim // 32)
+        total = 2 * (16 * n + 2 * n + n // 2)
+        buf = (ctypes.c_ubyte * max(1, total))()
+        _check(lib().spectra_kv_export(self.handle, buf, total))
+        return bytes(buf)[:total]
+
+    def close(self) -> None:
+        if self.handle:
+            lib().spectra_kv_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def spectra_free(c: Container):

@@ -195,6 +195,56 @@ int spectra_gemm_grouped(const spectra_container* const* cs, int count, const vo
  * does not fit the kernel's LDS row buffer (K above about 50000). */
 int spectra_embed(const spectra_container* c, const void* ids, int64_t T, void* out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Group-32 4-bit KV cache (SPECTRA page, abstract: the key-value cache is kept
+ * in microscaled Group-32 4-bit form).  One cache holds the keys and values of
+ * one attention layer for up to `capacity` tokens, `heads` cache heads of
+ * `head_dim` channels (64, 128 or 256).  Each head vector is quantized on
+ * append exactly as a bulk weight group per 32 consecutive channels (range
+ * [min(0, min), max(0, max)], s16 = fp16(range / 15), z = rint(-lo / s16),
+ * q = clamp(rint(w / s16) + z, 0, 15), in binary64), with no heavy-tailed
+ * split.  The handle is opaque, owns its device memory (on the device current
+ * at creation) and tracks its length on the host.
+ * ------------------------------------------------------------------------- */
+typedef struct spectra_kv spectra_kv;
+
+/* NULL on error (E_INVAL for shapes, E_NOMEM). */
+spectra_kv* spectra_kv_create(int64_t capacity, int32_t heads, int32_t head_dim);
+
+/* Quantize T new tokens and store them at positions [length, length + T).
+ * k, v: DEVICE fp16 [T][heads][head_dim], 16-byte aligned, finite values (a
+ * non-finite value leaves its group unspecified, never out of bounds).
+ * E_INVAL if length + T would exceed the capacity.  Enqueued on `stream`;
+ * the length grows at once on the host. */
+int spectra_kv_append(spectra_kv* kv, const void* k, const void* v, int64_t T, void* stream);
+
+/* Decode-step attention over the `length` cached tokens:
+ *   out[h] = softmax(q[h] K_hat^T / sqrt(head_dim)) V_hat,  h < q_heads,
+ * query head h reading cache head h / (q_heads / heads); K_hat, V_hat are the
+ * dequantized cache ((q - z) * s16).  q: DEVICE fp16 [q_heads][head_dim];
+ * out: DEVICE fp16 [q_heads][head_dim]; both 4-byte aligned.  q_heads must be
+ * a multiple of heads with at most 16 query heads per cache head; length >= 1
+ * (E_INVAL otherwise) and at most 524288 (E_UNSUPPORTED).
+ * Per element, |out - ref| <= 1e-3 * (sum_t p_t |V_hat[t]|) + 1e-6 with ref
+ * and p in binary64.  Uses the per-stream workspace (4 * q_heads * (length +
+ * (head_dim + 2) * ceil(length / 128)) bytes); enqueued on `stream`. */
+int spectra_kv_attend(const spectra_kv* kv, const void* q, int32_t q_heads, void* out, void* stream);
+
+/* Tokens currently cached (-1 for an invalid handle). */
+int64_t spectra_kv_length(const spectra_kv* kv);
+
+/* Forget every cached token (length 0); the memory is kept. */
+int spectra_kv_reset(spectra_kv* kv);
+
+/* Copy the first `length` tokens' quantized data to HOST memory, for
+ * bit-exact checks: K records, K scales, K zero bytes, then the same for V,
+ * each section [length][heads][G] in the device order (zeros [length][heads]
+ * [G/2]); 2 * length * heads * G * (16 + 2 + 1/2) bytes.  Synchronous. */
+int spectra_kv_export(const spectra_kv* kv, void* host_dst, uint64_t cap);
+
+/* Release the cache.  NULL-safe; unknown or freed handles are ignored. */
+void spectra_kv_free(spectra_kv* kv);
+
 /* Release the container and its device memory.  NULL-safe; freeing a handle
  * twice, or one this library did not return, does nothing.  Handles are
  * checked against the library's set of live containers, so any later call
