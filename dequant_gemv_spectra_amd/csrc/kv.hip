@@ -15,14 +15,12 @@
 // 256), so a byte never spans two vectors.
 //
 // Attention (one query per head, Hq = rep * H query heads, head h reading
-// cache head h / rep), three launches:
-//   k_kv_scores  one thread per cached token and cache head: dequantize the
-//                key (exact fp16 (q - z) pairs, as in the GEMV), dot it with
-//                the rep queries of that head in fp32, times s16 per group,
-//                divided by sqrt(D) -> scores [Hq][L] in the workspace;
-//   k_kv_pv      per (split of 128 tokens, query head): the split's max m,
-//                sum of exp(s - m) and sum_t exp(s_t - m) v_t with
-//                lane-per-channel-pair dequantization -> fp32 partials;
+// cache head h / rep), two launches:
+//   k_kv_split   per (split of 128 tokens, cache head): scores of the rep
+//                query heads from keys dequantized to exact fp16 (q - z)
+//                pairs (as in the GEMV), the split's max m and sum of
+//                exp(s - m), and sum_t exp(s_t - m) v_t with lane-per-channel-
+//                pair dequantization of the values -> fp32 partials;
 //   k_kv_combine rescales the splits to the global max and divides, fp16.
 #include "spectra_internal.h"
 #include "g32.h"
@@ -31,7 +29,6 @@ namespace spectra {
 namespace {
 
 constexpr int kGroup32 = 32;
-constexpr int kScoreThreads = 256;
 constexpr int kPvThreads = 256;
 constexpr int kTokensPerSplit = 128;
 constexpr int kMaxRep = 16;  // query heads per cache head handled in one pass
@@ -118,55 +115,6 @@ __device__ __forceinline__ half2_t pair_qz(uint32_t w, int j, uint32_t z) {
   return as_h2((ww & 0x000F000Fu) | 0x64006400u) - as_h2((0x6400u + z) * 0x00010001u);
 }
 
-// scores[hq][t] = q_hq . k_t / sqrt(D), hq = h * rep + r.
-template <int G>
-__global__ __launch_bounds__(kScoreThreads) void k_kv_scores(const KvView c, const uint16_t* __restrict__ q,
-                                                             int rep, int64_t L, float* __restrict__ scores) {
-  constexpr int D = 32 * G;
-  __shared__ half2_t qs[kMaxRep][D / 2];
-  const int h = blockIdx.y;
-  const int H = c.H;
-  for (int i = threadIdx.x; i < rep * D / 2; i += blockDim.x) {
-    const int rr = i / (D / 2), j = i % (D / 2);
-    qs[rr][j] = as_h2(reinterpret_cast<const uint32_t*>(q + (int64_t)(h * rep + rr) * D)[j]);
-  }
-  __syncthreads();
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= L) return;
-  const int64_t flat0 = (t * H + h) * G;
-  float acc[kMaxRep];
-#pragma unroll
-  for (int rr = 0; rr < kMaxRep; ++rr) acc[rr] = 0.f;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint4 rec = c.k.codes[flat0 + g];
-    const float sc = h2f(c.k.scales[flat0 + g]);
-    const uint32_t z = (c.k.zeros[(flat0 + g) >> 1] >> (4 * (g & 1))) & 0xFu;
-    const uint32_t w[4] = {rec.x, rec.y, rec.z, rec.w};
-    half2_t wq[16];
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wq[4 * d + j] = pair_qz(w[d], j, z);
-#pragma unroll
-    for (int rr = 0; rr < kMaxRep; ++rr) {  // unrolled so acc stays in registers
-      if (rr < rep) {
-        float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          a0 = __builtin_amdgcn_fdot2(wq[j], qs[rr][16 * g + j], a0, false);
-          a1 = __builtin_amdgcn_fdot2(wq[j + 1], qs[rr][16 * g + j + 1], a1, false);
-        }
-        acc[rr] = __builtin_fmaf(sc, a0 + a1, acc[rr]);
-      }
-    }
-  }
-  const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
-#pragma unroll
-  for (int rr = 0; rr < kMaxRep; ++rr)
-    if (rr < rep) scores[(int64_t)(h * rep + rr) * L + t] = acc[rr] * inv_sqrt_d;
-}
-
 __device__ __forceinline__ float block_max(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -189,90 +137,180 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-// Per (split of the tokens, query head): the split's max score m, l = sum_t
-// exp(s_t - m) and the partial sum_t exp(s_t - m) v_t, in fp32.  Lane l of a
-// wave owns channel pairs l + 64 i (i < D / 128; lanes < 32 for D = 64); each
-// wave takes every WAVES-th token of the split, kUnroll tokens per step with
-// all their loads issued before any is used (one step per wave at D <= 128).
-template <int G>
-__global__ __launch_bounds__(kPvThreads) void k_kv_pv(const KvView c, const float* __restrict__ scores,
-                                                      int rep, int64_t L, float* __restrict__ part,
-                                                      float* __restrict__ stats) {
+// One block per (split of kTokensPerSplit tokens, cache head h), serving the
+// rep query heads that read h:
+//   1. the value records of the split are requested first (lane-per-channel-
+//      pair: lane l owns pairs l + 64 i; each wave every WAVES-th token);
+//   2. threads 0 .. 127 take one token each: dequantize its key (exact fp16
+//      (q - z) pairs), dot it with the rep queries in fp32, times s16 per
+//      group, over sqrt(D) -> scores in LDS;
+//   3. per query head the split's max m and l = sum exp(s - m); the scores
+//      become p = exp(s - m);
+//   4. sum_t p_t v_t per query head in registers, reduced across the waves
+//      -> fp32 partials and (m, l) per (split, query head).
+// The keys and values of the split are read once for all rep query heads.
+template <int G, int REP>
+__global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const uint16_t* __restrict__ q,
+                                                         int64_t L, float* __restrict__ part,
+                                                         float* __restrict__ stats) {
+  constexpr int rep = REP;
   constexpr int D = 32 * G;
   constexpr int NP = D / 2;                   // channel pairs
   constexpr int PL = NP >= 64 ? NP / 64 : 1;  // pairs per lane
   constexpr int WAVES = kPvThreads / 64;
-  constexpr int kUnroll = kTokensPerSplit / WAVES / PL;  // 32 tokens per step (16 at D = 256)
-  __shared__ float red[WAVES];
+  constexpr int TS = kTokensPerSplit;
+  constexpr int UN = TS / WAVES;              // tokens per wave
+  constexpr int STEPS = PL;                   // value loads in STEPS rounds of UNS tokens
+  constexpr int UNS = UN / STEPS;
+  __shared__ half2_t qs[REP][D / 2];
+  __shared__ float sc[REP][TS];
+  __shared__ float mst[REP], lst[REP];
   __shared__ float pacc[WAVES][D];
-  const int split = blockIdx.x, hq = blockIdx.y;
-  const int h = hq / rep, H = c.H;
-  const float* srow = scores + (int64_t)hq * L;
-  const int64_t t0 = (int64_t)split * kTokensPerSplit;
-  const int64_t t1 = t0 + kTokensPerSplit < L ? t0 + kTokensPerSplit : L;
-  float m = -INFINITY;
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) m = fmaxf(m, srow[t]);
-  m = block_max(m, red);
-  float se = 0.f;
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) se += __expf(srow[t] - m);
-  se = block_sum(se, red);
-
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int H = c.H, Hq = H * rep;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float a[PL][2];
+  const int64_t t0 = (int64_t)split * TS;
+  for (int i = threadIdx.x; i < rep * D / 2; i += blockDim.x) {
+    const int rr = i / (D / 2), j = i % (D / 2);
+    qs[rr][j] = as_h2(reinterpret_cast<const uint32_t*>(q + (int64_t)(h * rep + rr) * D)[j]);
+  }
+
+  // 1. value loads of this wave's first UNS tokens (tokens past L read token t0's)
+  uint32_t vw[UNS][PL], vz[UNS][PL];
+  uint16_t vs[UNS][PL];
+  auto load_v = [&](int step) {
 #pragma unroll
-  for (int i = 0; i < PL; ++i) a[i][0] = a[i][1] = 0.f;
-  for (int64_t tb = t0 + wave; tb < t1; tb += (int64_t)WAVES * kUnroll) {
-    uint32_t w[kUnroll][PL], zb[kUnroll][PL];
-    uint16_t sb[kUnroll][PL];
-    float p[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t t = tb + (int64_t)u * WAVES;
-      const bool in = t < t1;
-      const int64_t flat0 = ((in ? t : t0) * H + h) * G;
-      p[u] = in ? srow[t] : -INFINITY;
+    for (int u = 0; u < UNS; ++u) {
+      const int64_t t = t0 + wave + (int64_t)WAVES * (step * UNS + u);
+      const int64_t flat0 = ((t < L ? t : t0) * H + h) * G;
 #pragma unroll
       for (int i = 0; i < PL; ++i) {
         const int pi = (lane + 64 * i) % NP;  // lanes past NP (D = 64) read a valid pair, unused
         const int g = pi >> 4, e = (2 * pi) & 31;
-        w[u][i] = reinterpret_cast<const uint32_t*>(c.v.codes + flat0 + g)[e >> 3];
-        sb[u][i] = c.v.scales[flat0 + g];
-        zb[u][i] = c.v.zeros[(flat0 + g) >> 1];
+        vw[u][i] = reinterpret_cast<const uint32_t*>(c.v.codes + flat0 + g)[e >> 3];
+        vs[u][i] = c.v.scales[flat0 + g];
+        vz[u][i] = c.v.zeros[(flat0 + g) >> 1];
       }
     }
+  };
+  load_v(0);
+  __syncthreads();  // qs ready
+
+  // 2. scores: every key load of the token first, then the arithmetic
+  if (threadIdx.x < TS) {
+    const int tl = threadIdx.x;
+    const int64_t t = t0 + tl;
+    const int64_t flat0 = ((t < L ? t : t0) * H + h) * G;
+    uint4 krec[G];
+    uint16_t ksc[G];
+    uint8_t kzb[G / 2];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float pu = __expf(p[u] - m);  // 0 for tokens past the split
+    for (int g = 0; g < G; ++g) {
+      krec[g] = c.k.codes[flat0 + g];
+      ksc[g] = c.k.scales[flat0 + g];
+    }
+#pragma unroll
+    for (int g = 0; g < G; g += 2) kzb[g / 2] = c.k.zeros[(flat0 + g) >> 1];
+    float acc[REP];
+#pragma unroll
+    for (int rr = 0; rr < REP; ++rr) acc[rr] = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float s16 = h2f(ksc[g]);
+      const uint32_t z = ((uint32_t)kzb[g / 2] >> (4 * (g & 1))) & 0xFu;
+      const uint32_t w[4] = {krec[g].x, krec[g].y, krec[g].z, krec[g].w};
+      half2_t wq[16];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wq[4 * d + j] = pair_qz(w[d], j, z);
+#pragma unroll
+      for (int rr = 0; rr < REP; ++rr) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          a0 = __builtin_amdgcn_fdot2(wq[j], qs[rr][16 * g + j], a0, false);
+          a1 = __builtin_amdgcn_fdot2(wq[j + 1], qs[rr][16 * g + j + 1], a1, false);
+        }
+        acc[rr] = __builtin_fmaf(s16, a0 + a1, acc[rr]);
+      }
+    }
+    const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
+#pragma unroll
+    for (int rr = 0; rr < REP; ++rr) sc[rr][tl] = t < L ? acc[rr] * inv_sqrt_d : -INFINITY;
+  }
+  __syncthreads();
+
+  // 3. split max and exp sums, one query head per wave at a time
+  for (int rr = wave; rr < rep; rr += WAVES) {
+    float m = -INFINITY;
+    for (int j = lane; j < TS; j += 64) m = fmaxf(m, sc[rr][j]);
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float l = 0.f;
+    for (int j = lane; j < TS; j += 64) {
+      const float p = __expf(sc[rr][j] - m);  // 0 for tokens past L
+      sc[rr][j] = p;
+      l += p;
+    }
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+    if (lane == 0) {
+      mst[rr] = m;
+      lst[rr] = l;
+    }
+  }
+  __syncthreads();
+
+  // 4. values
+  float a[REP][PL][2];
+#pragma unroll
+  for (int rr = 0; rr < REP; ++rr)
+#pragma unroll
+    for (int i = 0; i < PL; ++i) a[rr][i][0] = a[rr][i][1] = 0.f;
+#pragma unroll
+  for (int step = 0; step < STEPS; ++step) {
+    if (step) load_v(step);
+#pragma unroll
+    for (int u = 0; u < UNS; ++u) {
+      const int tl = wave + WAVES * (step * UNS + u);
 #pragma unroll
       for (int i = 0; i < PL; ++i) {
         const int pi = (lane + 64 * i) % NP;
         const int g = pi >> 4, e = (2 * pi) & 31;
-        const uint32_t z = (zb[u][i] >> (4 * (g & 1))) & 0xFu;
-        const half2_t qz = pair_qz(w[u][i], (e & 7) >> 1, z);
-        const float sc = h2f(sb[u][i]);
-        a[i][0] = __builtin_fmaf(pu, (float)qz.x * sc, a[i][0]);
-        a[i][1] = __builtin_fmaf(pu, (float)qz.y * sc, a[i][1]);
+        const uint32_t z = (vz[u][i] >> (4 * (g & 1))) & 0xFu;
+        const half2_t qz = pair_qz(vw[u][i], (e & 7) >> 1, z);
+        const float s16 = h2f(vs[u][i]);
+        const float v0 = (float)qz.x * s16, v1 = (float)qz.y * s16;
+#pragma unroll
+        for (int rr = 0; rr < REP; ++rr) {
+          const float p = sc[rr][tl];
+          a[rr][i][0] = __builtin_fmaf(p, v0, a[rr][i][0]);
+          a[rr][i][1] = __builtin_fmaf(p, v1, a[rr][i][1]);
+        }
       }
     }
   }
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int pi = lane + 64 * i;
-    if (pi < NP) {
-      pacc[wave][2 * pi] = a[i][0];
-      pacc[wave][2 * pi + 1] = a[i][1];
+  for (int rr = 0; rr < REP; ++rr) {
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int pi = lane + 64 * i;
+      if (pi < NP) {
+        pacc[wave][2 * pi] = a[rr][i][0];
+        pacc[wave][2 * pi + 1] = a[rr][i][1];
+      }
     }
-  }
-  __syncthreads();
-  const int64_t base = (int64_t)split * gridDim.y + hq;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float sum = 0.f;
-    for (int w2 = 0; w2 < WAVES; ++w2) sum += pacc[w2][d];
-    part[base * D + d] = sum;
-  }
-  if (threadIdx.x == 0) {
-    stats[2 * base] = m;
-    stats[2 * base + 1] = se;
+    __syncthreads();
+    const int64_t base = (int64_t)split * Hq + h * rep + rr;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+      float sum = 0.f;
+      for (int w2 = 0; w2 < WAVES; ++w2) sum += pacc[w2][d];
+      part[base * D + d] = sum;
+    }
+    if (threadIdx.x == 0) {
+      stats[2 * base] = mst[rr];
+      stats[2 * base + 1] = lst[rr];
+    }
+    __syncthreads();
   }
 }
 
@@ -320,29 +358,38 @@ int64_t kv_max_attend_length() { return (int64_t)kMaxSplits * kTokensPerSplit; }
 
 namespace {
 
-template <int G>
-hipError_t attend_g(const KvView& c, const uint16_t* q, int rep, int64_t L, uint16_t* out, void* ws,
-                    hipStream_t s) {
+template <int G, int REP>
+hipError_t attend_gr(const KvView& c, const uint16_t* q, int64_t L, uint16_t* out, void* ws, hipStream_t s) {
   constexpr int D = 32 * G;
-  const int Hq = c.H * rep;
+  const int Hq = c.H * REP;
   const int64_t splits = splits_of(L);
-  float* scores = static_cast<float*>(ws);
-  float* part = scores + (size_t)Hq * L;
+  float* part = static_cast<float*>(ws);
   float* stats = part + (size_t)splits * Hq * D;
-  hipLaunchKernelGGL(k_kv_scores<G>, dim3((unsigned)((L + kScoreThreads - 1) / kScoreThreads), (unsigned)c.H),
-                     dim3(kScoreThreads), 0, s, c, q, rep, L, scores);
-  hipLaunchKernelGGL(k_kv_pv<G>, dim3((unsigned)splits, (unsigned)Hq), dim3(kPvThreads), 0, s, c, scores, rep, L,
+  hipLaunchKernelGGL((k_kv_split<G, REP>), dim3((unsigned)splits, (unsigned)c.H), dim3(kPvThreads), 0, s, c, q, L,
                      part, stats);
   hipLaunchKernelGGL(k_kv_combine, dim3((unsigned)Hq), dim3(D < 256 ? D : 256), 0, s, part, stats, (int)splits,
                      Hq, D, out);
   return hipGetLastError();
 }
 
+template <int G>
+hipError_t attend_g(const KvView& c, const uint16_t* q, int rep, int64_t L, uint16_t* out, void* ws,
+                    hipStream_t s) {
+  switch (rep) {
+    case 1: return attend_gr<G, 1>(c, q, L, out, ws, s);
+    case 2: return attend_gr<G, 2>(c, q, L, out, ws, s);
+    case 4: return attend_gr<G, 4>(c, q, L, out, ws, s);
+    case 8: return attend_gr<G, 8>(c, q, L, out, ws, s);
+    case 16: return attend_gr<G, 16>(c, q, L, out, ws, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
 }  // namespace
 
 size_t kv_attend_workspace_bytes(const KvView& c, int rep, int64_t L) {
   const int64_t Hq = (int64_t)c.H * rep;
-  return 4 * (size_t)(Hq * L + splits_of(L) * Hq * (c.D + 2));
+  return 4 * (size_t)(splits_of(L) * Hq * (c.D + 2));
 }
 
 bool kv_shape_supported(int64_t heads, int64_t head_dim) {

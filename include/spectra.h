@@ -226,8 +226,8 @@ int spectra_kv_append(spectra_kv* kv, const void* k, const void* v, int64_t T, v
  * a multiple of heads with at most 16 query heads per cache head; length >= 1
  * (E_INVAL otherwise) and at most 524288 (E_UNSUPPORTED).
  * Per element, |out - ref| <= 1e-3 * (sum_t p_t |V_hat[t]|) + 1e-6 with ref
- * and p in binary64.  Uses the per-stream workspace (4 * q_heads * (length +
- * (head_dim + 2) * ceil(length / 128)) bytes); enqueued on `stream`. */
+ * and p in binary64.  Uses the per-stream workspace (4 * q_heads *
+ * (head_dim + 2) * ceil(length / 128) bytes); enqueued on `stream`. */
 int spectra_kv_attend(const spectra_kv* kv, const void* q, int32_t q_heads, void* out, void* stream);
 
 /* Tokens currently cached (-1 for an invalid handle). */
