@@ -333,12 +333,15 @@ __device__ __forceinline__ void load_frag(Frag<P, U, OS>& f, const DeviceView& v
 }
 
 // y rows m < M of the tile: MX rows of x share each dequantized record.
-template <int L, int P, int U, int OS, int MX>
+// XR: one row of x, held in registers for this lane's groups (xreg) instead
+// of read from LDS per tile.
+template <int L, int P, int U, int OS, int MX, bool XR>
 __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const DeviceView& v,
                                              int64_t row0, int64_t row_end, int lt, int team,
                                              const uint16_t* xs, int xstride,
                                              const float (&xor_)[MX][OS], int M,
-                                             uint16_t* __restrict__ y, const Nib nb) {
+                                             uint16_t* __restrict__ y, const Nib nb,
+                                             const half2_t (&xreg)[P][16]) {
   constexpr int T = kBlock / L;
   const int G = v.G, n_out = v.n_out;
   // The x slots are the same for every tile.  With several rows of x the
@@ -362,9 +365,13 @@ __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const Devi
       const uint32_t z = (f.z[u][p] >> (4u * odd)) & 0xFu;
       const float sc = h2f((uint16_t)f.s[u][p]);
       if constexpr (MX == 1) {
-        half2_t xr[16];
-        read_x(xs + slot, xr);
-        acc[0][u] = __builtin_fmaf(sc, group_dot(f.c[u][p], z, xr, nb), acc[0][u]);
+        if constexpr (XR) {
+          acc[0][u] = __builtin_fmaf(sc, group_dot(f.c[u][p], z, xreg[p], nb), acc[0][u]);
+        } else {
+          half2_t xr[16];
+          read_x(xs + slot, xr);
+          acc[0][u] = __builtin_fmaf(sc, group_dot(f.c[u][p], z, xr, nb), acc[0][u]);
+        }
       } else {
         half2_t wq[16];
         dequant_record(f.c[u][p], z ^ slot_dep, nb, wq);
@@ -440,6 +447,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   // The first tile's weights are requested right behind the x and perm
   // loads, so their HBM latency overlaps the gather and the barriers.
   Frag<P, U, OS> fa, fb;
+  half2_t xreg[P][16];  // used by the long loop with one row of x
   stage_x<MX>(v, task.x, tasks.m_rows, xs, xstride, xraw, tid, [&] {
     __builtin_amdgcn_sched_barrier(0);
     load_frag<L, P, U, OS>(fa, v, row, end, lt, team);
@@ -470,16 +478,30 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
       if (t + 1 < NT) load_frag<L, P, U, OS>(nxt, v, row + (t + 1) * stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
       if (row + t * stride < end)
-        compute_frag<L, P, U, OS, MX>(cur, v, row + t * stride, end, lt, team, xs, xstride, xor_, tasks.m_rows, task.y, nb);
+        compute_frag<L, P, U, OS, MX, false>(cur, v, row + t * stride, end, lt, team, xs, xstride, xor_, tasks.m_rows,
+                                             task.y, nb, xreg);
     }
   } else {
+    // One row of x: this lane's groups of x stay in registers across the
+    // tiles (the long loop reads them from LDS once instead of per tile).
+    constexpr bool XR = MX == 1 && P <= 5;  // 16 registers per slot: more would spill
+    if constexpr (XR) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int g = lt + L * p;
+        read_x(xs + (g < G ? g : 0) * kXSlot, xreg[p]);
+      }
+    }
     for (; row < v.N; row += 2 * stride) {
       load_frag<L, P, U, OS>(fb, v, row + stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      compute_frag<L, P, U, OS, MX>(fa, v, row, end, lt, team, xs, xstride, xor_, tasks.m_rows, task.y, nb);
+      compute_frag<L, P, U, OS, MX, XR>(fa, v, row, end, lt, team, xs, xstride, xor_, tasks.m_rows, task.y, nb,
+                                        xreg);
       load_frag<L, P, U, OS>(fa, v, row + 2 * stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      if (row + stride < v.N) compute_frag<L, P, U, OS, MX>(fb, v, row + stride, end, lt, team, xs, xstride, xor_, tasks.m_rows, task.y, nb);
+      if (row + stride < v.N)
+        compute_frag<L, P, U, OS, MX, XR>(fb, v, row + stride, end, lt, team, xs, xstride, xor_, tasks.m_rows, task.y,
+                                          nb, xreg);
     }
   }
 }
@@ -524,29 +546,17 @@ int batch_tile(int64_t M) { return M <= 1 ? 1 : (M == 2 ? 2 : 4); }
 constexpr int kU = SPECTRA_GEMV_U;
 constexpr int64_t kPipeTiles = 6;  // tiles per block from which the loop without early exits pays
 
-// Split the block budget between the tasks in proportion to their rows.
-template <int L, int P, int MX>
-int64_t plan_blocks(GemvTasks& ts, size_t lds) {
-  constexpr int64_t kTileRows = (int64_t)(kBlock / L) * kU;
+// Split a budget of per_cu blocks per CU between the tasks in proportion to
+// their rows.
+int64_t plan_blocks(GemvTasks& ts, int64_t per_cu) {
   int64_t total_rows = 0;
   for (int i = 0; i < ts.count; ++i) total_rows += ts.t[i].v.N;
-  // Launches long enough to give every block several tiles run two blocks
-  // per CU (16 waves, so one wave's dequant work overlaps another's loads);
-  // short ones keep one block, whose x staging is then paid once per CU.
-  // Two blocks fit only while a lane needs at most 128 registers, which
-  // holds for one row of x and up to four slots per lane, and the LDS of
-  // two blocks fits the CU's 160 KiB.
-  int64_t all_tiles = 0;
-  for (int i = 0; i < ts.count; ++i) all_tiles += (ts.t[i].v.N + kTileRows - 1) / kTileRows;
-  const int64_t cus = ts.t[0].v.cu_count;
-  const bool two = MX == 1 && P <= 4 && 2 * lds <= (size_t)160 * 1024 &&
-                   all_tiles >= cus * 2 * SPECTRA_GEMV_TWO_BLOCK_TILES;
-  const int64_t budget = cus * (two ? 2 : SPECTRA_GEMV_BLOCKS_PER_CU);
+  const int64_t budget = (int64_t)ts.t[0].v.cu_count * per_cu;
   int64_t begin = 0;
   for (int i = 0; i < ts.count; ++i) {
     GemvTask& t = ts.t[i];
     // more blocks than whole tiles is fine: short launches then give every
-    // block a partial tile (rows_per_block below kTileRows)
+    // block a partial tile (rows_per_block below the tile)
     int64_t blocks = (budget * t.v.N + total_rows - 1) / total_rows;
     if (blocks > t.v.N) blocks = t.v.N;
     if (blocks < 1) blocks = 1;
@@ -571,18 +581,30 @@ hipError_t launch_k(dim3 grid, size_t lds, hipStream_t s, const GemvTasks& ts) {
 template <int L, int P, int MX>
 hipError_t launch_lp(GemvTasks& ts, size_t lds, hipStream_t s) {
   constexpr int64_t kTileRows = (int64_t)(kBlock / L) * kU;
-  const int64_t blocks = plan_blocks<L, P, MX>(ts, lds);
-  int64_t most = 0;  // most tiles any block walks when blocks take whole tiles in turn
+  int64_t blocks = plan_blocks(ts, SPECTRA_GEMV_BLOCKS_PER_CU);
+  int64_t most = 0, all_tiles = 0;  // most tiles any block walks when blocks take whole tiles in turn
   for (int i = 0; i < ts.count; ++i) {
     const int64_t tiles = (ts.t[i].v.N + kTileRows - 1) / kTileRows;
     const int64_t per = (tiles + ts.t[i].nblocks - 1) / ts.t[i].nblocks;
     most = per > most ? per : most;
+    all_tiles += tiles;
+  }
+  if (MX > 1 || most >= kPipeTiles) {  // batch tiles always take the loop form
+    // Long launches run a second block per CU (16 waves: one wave's dequant
+    // work overlaps another's loads) when two fit, registers and LDS as the
+    // occupancy calculator counts them, and every block still walks several
+    // tiles.
+    if (all_tiles >= (int64_t)ts.t[0].v.cu_count * 2 * SPECTRA_GEMV_TWO_BLOCK_TILES) {
+      int fit = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &fit, reinterpret_cast<const void*>(&k_gemv_m1<L, P, kU, 0, MX>), kBlock, lds) == hipSuccess &&
+          fit >= 2)
+        blocks = plan_blocks(ts, 2);
+    }
+    for (int i = 0; i < ts.count; ++i) ts.t[i].rows_per_block = 0;
+    return launch_k<L, P, 0, MX>(dim3((unsigned)blocks), lds, s, ts);
   }
   const dim3 grid((unsigned)blocks);
-  if (MX > 1 || most >= kPipeTiles) {  // batch tiles always take the loop form
-    for (int i = 0; i < ts.count; ++i) ts.t[i].rows_per_block = 0;
-    return launch_k<L, P, 0, MX>(grid, lds, s, ts);
-  }
   // Short launch: equal row ranges per block, at most nt tiles each.
   int64_t nt = 1;
   for (int i = 0; i < ts.count; ++i) {
