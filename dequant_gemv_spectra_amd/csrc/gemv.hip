@@ -547,22 +547,36 @@ constexpr int kU = SPECTRA_GEMV_U;
 constexpr int64_t kPipeTiles = 6;  // tiles per block from which the loop without early exits pays
 
 // Split a budget of per_cu blocks per CU between the tasks in proportion to
-// their rows.
+// their rows, never past the budget (one block over it would run as a second
+// round on some CU and cost the launch a whole extra block's time).
 int64_t plan_blocks(GemvTasks& ts, int64_t per_cu) {
   int64_t total_rows = 0;
   for (int i = 0; i < ts.count; ++i) total_rows += ts.t[i].v.N;
   const int64_t budget = (int64_t)ts.t[0].v.cu_count * per_cu;
-  int64_t begin = 0;
+  int64_t nb[kMaxTasks], used = 0;
   for (int i = 0; i < ts.count; ++i) {
-    GemvTask& t = ts.t[i];
     // more blocks than whole tiles is fine: short launches then give every
     // block a partial tile (rows_per_block below the tile)
-    int64_t blocks = (budget * t.v.N + total_rows - 1) / total_rows;
-    if (blocks > t.v.N) blocks = t.v.N;
-    if (blocks < 1) blocks = 1;
-    t.block_begin = (int32_t)begin;
-    t.nblocks = (int32_t)blocks;
-    begin += blocks;
+    int64_t b = budget * ts.t[i].v.N / total_rows;
+    if (b > ts.t[i].v.N) b = ts.t[i].v.N;
+    if (b < 1) b = 1;
+    nb[i] = b;
+    used += b;
+  }
+  for (bool grew = true; used < budget && grew;) {  // hand out what flooring left over
+    grew = false;
+    for (int i = 0; i < ts.count && used < budget; ++i)
+      if (nb[i] < ts.t[i].v.N) {
+        ++nb[i];
+        ++used;
+        grew = true;
+      }
+  }
+  int64_t begin = 0;
+  for (int i = 0; i < ts.count; ++i) {
+    ts.t[i].block_begin = (int32_t)begin;
+    ts.t[i].nblocks = (int32_t)nb[i];
+    begin += nb[i];
   }
   return begin;
 }
