@@ -69,16 +69,20 @@ struct GemvTask {
   DeviceView v;
   const uint16_t* x;
   uint16_t* y;
-  int32_t block_begin;  // first block of this task in the grid
-  int32_t nblocks;      // blocks serving this task
+  int32_t nblocks;         // blocks serving this task
   int32_t rows_per_block;  // contiguous rows per block (short launches), else 0
 };
 
+// Kernel arguments.  A block finds its task from `begin` alone (one batch of
+// scalar loads, unrolled over every entry) and then reads that task's fields
+// in a second batch: two dependent round trips to the argument memory before
+// its first vector load, each of which costs on the order of 0.5 us.
 struct GemvTasks {
-  GemvTask t[kMaxTasks];
+  int32_t begin[kMaxTasks];  // first block of each task; INT32_MAX past the last task
   int32_t count;
   uint32_t nib_lo, nib_hi, mag_lo, mag_hi;  // see Nib
   int32_t m_rows;                           // rows of x (and y) of the launch, <= MX
+  GemvTask t[kMaxTasks];
 };
 
 template <int CTRL>
@@ -422,10 +426,19 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   constexpr int T = kBlock / L;          // teams per block
   constexpr int kTileRows = T * U;
   extern __shared__ __align__(16) unsigned char smem[];
-  int ti = 0;
-  for (int i = 1; i < tasks.count; ++i)
-    if ((int32_t)blockIdx.x >= tasks.t[i].block_begin) ti = i;
+  int ti = 0, first = 0;  // the block's task and that task's first block
+#pragma unroll
+  for (int i = 1; i < kMaxTasks; ++i)
+    if ((int32_t)blockIdx.x >= tasks.begin[i]) {
+      ti = i;
+      first = tasks.begin[i];
+    }
   const GemvTask& task = tasks.t[ti];
+  // Every field of the task in scalar registers at once: used one by one,
+  // the compiler spreads their loads over several dependent round trips.
+  asm volatile("" ::"s"(task.v.codes), "s"(task.v.scales), "s"(task.v.zeros), "s"(task.v.outliers),
+               "s"(task.v.perm), "s"(task.x), "s"(task.y), "s"(task.v.N), "s"(task.v.K), "s"(task.v.K_b),
+               "s"(task.v.G), "s"(task.v.n_out), "s"(task.nblocks), "s"(task.rows_per_block));
   uint32_t mlo, mhi;  // opaque copies: the compiler cannot fold them back into literals
   asm volatile("v_mov_b32 %0, %1" : "=v"(mlo) : "s"(tasks.mag_lo));
   asm volatile("v_mov_b32 %0, %1" : "=v"(mhi) : "s"(tasks.mag_hi));
@@ -438,7 +451,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   const int tid = threadIdx.x;
   const int lt = tid % L;
   const int team = tid / L;
-  const int64_t lb = (int64_t)(blockIdx.x - task.block_begin);
+  const int64_t lb = (int64_t)((int32_t)blockIdx.x - first);
   // NT >= 1: rows [row, end) in tiles of kTileRows; NT == 0: tiles `stride` apart
   const int64_t stride = NT ? (int64_t)kTileRows : (int64_t)task.nblocks * kTileRows;
   int64_t row = NT ? lb * task.rows_per_block : lb * kTileRows;
@@ -573,10 +586,12 @@ int64_t plan_blocks(GemvTasks& ts, int64_t per_cu) {
       }
   }
   int64_t begin = 0;
-  for (int i = 0; i < ts.count; ++i) {
-    ts.t[i].block_begin = (int32_t)begin;
-    ts.t[i].nblocks = (int32_t)nb[i];
-    begin += nb[i];
+  for (int i = 0; i < kMaxTasks; ++i) {
+    ts.begin[i] = i < ts.count ? (int32_t)begin : INT32_MAX;
+    if (i < ts.count) {
+      ts.t[i].nblocks = (int32_t)nb[i];
+      begin += nb[i];
+    }
   }
   return begin;
 }
