@@ -303,6 +303,256 @@ __global__ __launch_bounds__(64 * kMaxW) void k_mfma(const DeviceView v, const u
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// k_mfma_ks: the batched product for 1 <= M <= 16 when M rows of x fit in
+// LDS.  k_mfma gives each wave 16 rows for the whole K loop, so at any moment
+// the chip reads a few records of every row of the matrix: a column-wise
+// sweep that opens many DRAM pages for a few bytes each.  Here a block owns a
+// tile of 16 consecutive rows at a time (one contiguous stretch of the code
+// section) and its 8 waves split the tile's groups between them: wave w takes
+// quads of groups w*Q .. w*Q + Q - 1 (a quad is 4 consecutive groups).  Blocks
+// walk the tiles b, b + B, b + 2B, ..., so the chip streams one moving window
+// of the matrix, as the GEMV does.
+//
+// Lane (r, c) (r = lane / 16, c = lane % 16) loads the whole record of row c,
+// group 4q + r (16 bytes).  A 4 x 4 transpose across the lane quarters and the
+// four words (v_permlane32_swap and v_permlane16_swap) leaves lane (r, c)
+// holding word r of the records of row c for the four groups of the quad: the
+// B operand of v_mfma_f32_16x16x32_f16 (members 8r .. 8r + 7 of row c) for
+// each group.  Scales and zero bytes are loaded row-contiguously instead
+// (consecutive lanes on consecutive groups of a row: a few cache lines per
+// instruction, where one scale per record lane would touch 16 rows) and pass
+// through a small wave-private LDS area, from which lane (r, c) reads the four
+// scales and zero bytes of row c and the quad.  Each group's product goes into
+// a zero accumulator and is added with its fp32 scale, as in k_mfma.  The A
+// operand is x in bulk order, read from LDS; lanes of rows m >= M read row
+// M - 1, and those output rows are never stored.
+// Each wave then holds a partial 16 x 16 product; the waves add theirs through
+// LDS (two alternating buffers, one barrier per tile) and M * 16 threads write
+// the tile's outputs.  Heavy-tailed columns: wave w takes the 32-column blocks
+// w and w + 8 of the fp16 outlier matrix.
+constexpr int kKsWaves = 8;
+constexpr int kKsThreads = 64 * kKsWaves;
+constexpr int kKsXSeg = 24;    // 16-byte x segments per thread staged in one round trip
+constexpr int kKsMaxQ = 10;    // quads per wave (G <= 320); more would spill registers
+constexpr int kStreamNt = 2;   // cache-policy bit nt on code records (read once)
+
+template <int Q, int OB>
+struct KsFrag {
+  u32x4 c[Q];
+  uint32_t s[Q], z[Q];  // scale and zero byte of element 64 i + lane of the wave's 16 x 4Q groups
+  // 8 fp16 heavy-tailed weights per outlier block, one per register until
+  // the tile is computed: packing them at load time would wait for the loads
+  uint32_t o[OB > 0 ? OB : 1][8];
+};
+
+// Lane (r, c) register j <- lane (j, c) register r, for r, j < 4.
+__device__ __forceinline__ void transpose4(uint32_t& a0, uint32_t& a1, uint32_t& a2, uint32_t& a3) {
+  auto p = __builtin_amdgcn_permlane32_swap(a0, a2, false, false);
+  a0 = p[0];
+  a2 = p[1];
+  p = __builtin_amdgcn_permlane32_swap(a1, a3, false, false);
+  a1 = p[0];
+  a3 = p[1];
+  p = __builtin_amdgcn_permlane16_swap(a0, a1, false, false);
+  a0 = p[0];
+  a1 = p[1];
+  p = __builtin_amdgcn_permlane16_swap(a2, a3, false, false);
+  a2 = p[0];
+  a3 = p[1];
+}
+
+// Wave-private metadata rows: 4Q groups + 4 of padding (keeps the 8-byte
+// reads aligned and spreads the 16 rows over the banks).
+constexpr int ks_meta_stride(int Q) { return 4 * Q + 4; }
+constexpr int ks_meta_bytes(int Q) { return 16 * ks_meta_stride(Q) * 3; }  // u16 scales, then u8 zeros
+
+size_t ks_lds_bytes(int KW, int64_t M, int Q) {
+  const size_t mr = (size_t)((M + 3) / 4);
+  return (size_t)M * ((size_t)KW + 8) * 2 + 2 * kKsWaves * 16 * mr * 16 + (size_t)kKsWaves * ks_meta_bytes(Q);
+}
+
+template <int Q, int OB>
+__global__ __launch_bounds__(kKsThreads) void k_mfma_ks(const DeviceView v, const uint16_t* __restrict__ xw,
+                                                        int KW, int M, uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r4 = lane >> 4, c = lane & 15;
+  const int G = v.G, n_out = v.n_out;
+  const int KP = 32 * G;
+  const int nob = (n_out + 31) >> 5;
+  const int RS = KW + 8;  // LDS row stride in halves: rows 16 bytes apart mod 128 (conflict-free reads)
+  const int MR = (M + 3) >> 2;
+  constexpr int MS = ks_meta_stride(Q);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  float4_t* part = reinterpret_cast<float4_t*>(smem + (size_t)M * RS * 2);  // [2][waves][16 * MR]
+  unsigned char* meta = reinterpret_cast<unsigned char*>(part + 2 * kKsWaves * 16 * MR) + w * ks_meta_bytes(Q);
+  uint16_t* ms = reinterpret_cast<uint16_t*>(meta);  // [16][MS] scales
+  unsigned char* mz = meta + 16 * MS * 2;            // [16][MS] zero bytes
+  const int64_t ntiles = (v.N + 15) / 16;
+  const int64_t B = gridDim.x;
+  int64_t tile = blockIdx.x;
+
+  auto load_tile = [&](KsFrag<Q, OB>& f, int64_t t) {
+    const int64_t row0 = t * 16;
+    const int64_t left = v.N - row0;
+    const int rows = left <= 0 ? 0 : (left < 16 ? (int)left : 16);
+    const int64_t i0 = (rows > 0 ? row0 : 0) * G;
+    const __amdgpu_buffer_rsrc_t rc = rsrc(v.codes + i0, (uint64_t)rows * G * 16);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(v.scales + i0, (uint64_t)rows * G * 2);
+    const int64_t zb0 = i0 >> 1;
+    const uint32_t i0odd = (uint32_t)(i0 & 1);
+    const __amdgpu_buffer_rsrc_t rz = rsrc(v.zeros + zb0, (uint64_t)(((i0 + (int64_t)rows * G + 1) >> 1) - zb0));
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int g = 4 * (w * Q + i) + r4;
+      const bool ok = g < G;  // a group past G would be the next row's
+      const uint32_t local = (uint32_t)(c * G + g);
+      f.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? local * 16u : kOob, 0, kStreamNt);
+    }
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int e = 64 * i + lane, row = e / (4 * Q), g = 4 * w * Q + e % (4 * Q);
+      const bool ok = g < G;
+      const uint32_t local = (uint32_t)(row * G + g);
+      f.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? local * 2u : kOob, 0, 0);
+      f.z[i] = __builtin_amdgcn_raw_buffer_load_b8(rz, ok ? (local + i0odd) >> 1 : kOob, 0, 0);
+    }
+    if constexpr (OB > 0) {
+      const __amdgpu_buffer_rsrc_t ro =
+          rsrc(v.outliers + (rows > 0 ? row0 : 0) * n_out, (uint64_t)rows * n_out * 2);
+#pragma unroll
+      for (int k = 0; k < OB; ++k) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 32 * (w + kKsWaves * k) + 8 * r4 + e;
+          f.o[k][e] = __builtin_amdgcn_raw_buffer_load_b16(ro, j < n_out ? (uint32_t)(c * n_out + j) * 2u : kOob, 0, 0);
+        }
+      }
+    }
+  };
+
+  // x rows in bulk order from the workspace: every thread's segments in one
+  // round trip, the block's first tile requested right behind them.
+  KsFrag<Q, OB> fa, fb;
+  {
+    const int segs_row = KW >> 3;
+    const int nseg = M * segs_row;
+    const __amdgpu_buffer_rsrc_t rx = rsrc(xw, (uint64_t)M * KW * 2);
+    u32x4 xv[kKsXSeg];
+#pragma unroll
+    for (int i = 0; i < kKsXSeg; ++i) {
+      if (i * kKsThreads >= nseg) break;  // block-uniform
+      const int s = tid + kKsThreads * i;
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, s < nseg ? (uint32_t)s * 16u : kOob, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(fa, tile);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kKsXSeg; ++i) {
+      if (i * kKsThreads >= nseg) break;
+      const int s = tid + kKsThreads * i;
+      if (s < nseg) {
+        const int m = s / segs_row, col = s - m * segs_row;
+        *reinterpret_cast<u32x4*>(xs + m * RS + 8 * col) = xv[i];
+      }
+    }
+  }
+  __syncthreads();
+
+  const uint16_t* xa = xs + (c < M ? c : M - 1) * RS + 8 * r4;  // this lane's A row (rows past M: not stored)
+  auto compute = [&](const KsFrag<Q, OB>& f, int64_t t) {
+    float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+    const uint32_t rowpar = (uint32_t)(((t * 16 + c) * (int64_t)G) & 1);  // flat index parity at group 0
+    // this tile's scales and zero bytes through the wave's LDS rows (the
+    // previous tile's reads come first in this wave's LDS order)
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int e = 64 * i + lane, row = e / (4 * Q), grp = e % (4 * Q);
+      ms[row * MS + grp] = (uint16_t)f.s[i];
+      mz[row * MS + grp] = (unsigned char)f.z[i];
+    }
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int gq = 4 * (w * Q + i);
+      if (gq >= G) break;  // wave-uniform
+      uint32_t R[4] = {f.c[i].x, f.c[i].y, f.c[i].z, f.c[i].w};
+      transpose4(R[0], R[1], R[2], R[3]);
+      const uint2 s4 = *reinterpret_cast<const uint2*>(ms + c * MS + 4 * i);
+      const uint32_t z4 = *reinterpret_cast<const uint32_t*>(mz + c * MS + 4 * i);
+      const uint32_t S[4] = {s4.x, s4.x >> 16, s4.y, s4.y >> 16};
+      float4_t p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (gq + j >= G) break;
+        const uint32_t par = (rowpar ^ (uint32_t)(gq + j)) & 1u;
+        const uint32_t z = (z4 >> (8u * j + 4u * par)) & 0xFu;
+        const half8 b = dequant_word(R[j], z);
+        const half8 a = *reinterpret_cast<const half8*>(xa + 32 * (gq + j));
+        p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (gq + j >= G) break;
+        acc += h2f((uint16_t)S[j]) * p[j];
+      }
+    }
+    if constexpr (OB > 0) {
+#pragma unroll
+      for (int k = 0; k < OB; ++k) {
+        const int ob = w + kKsWaves * k;
+        if (ob < nob) {
+          const half8 a = *reinterpret_cast<const half8*>(xa + KP + 32 * ob);
+          const uint32_t* o = f.o[k];
+          const half8 b = __builtin_bit_cast(
+              half8, u32x4{o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16)});
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+        }
+      }
+    }
+    return acc;
+  };
+  // Sum of the waves' partials for tile t: D lane (r, c) holds rows m = 4r + i
+  // of output column c; lanes r < MR carry the rows m < M.
+  auto reduce = [&](const float4_t acc, int64_t t, int buf) {
+    float4_t* pb = part + buf * kKsWaves * 16 * MR;
+    if (lane < 16 * MR) pb[w * 16 * MR + lane] = acc;
+    __syncthreads();
+    if (tid < 16 * M) {
+      const int m = tid >> 4, n = tid & 15;
+      const float* pf = reinterpret_cast<const float*>(pb) + ((m >> 2) * 16 + n) * 4 + (m & 3);
+      float sum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kKsWaves; ++ww) sum += pf[ww * 16 * MR * 4];
+      const int64_t row = t * 16 + n;
+      if (row < v.N) y[(int64_t)m * v.N + row] = f2h(sum);
+    }
+  };
+  // Two register buffers: a buffer is refilled as soon as its tile has been
+  // multiplied, before the barrier of the cross-wave sum, so two tiles stay in
+  // flight while the waves wait for one another; no early exit sits between a
+  // load and its use.
+  load_tile(fb, tile + B);
+  for (; tile < ntiles; tile += 2 * B) {
+    __builtin_amdgcn_sched_barrier(0);
+    float4_t acc = compute(fa, tile);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(fa, tile + 2 * B);
+    __builtin_amdgcn_sched_barrier(0);
+    reduce(acc, tile, 0);
+    // unconditional, so the wait counts are the same on every path (a tile
+    // past the end multiplies zeros and is not stored)
+    acc = compute(fb, tile + B);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(fb, tile + 3 * B);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tile + B < ntiles) reduce(acc, tile + B, 1);
+  }
+}
+
 }  // namespace
 
 bool mfma_supports(const DeviceView& v, int64_t M) {
@@ -346,6 +596,75 @@ void launch_mt(const DeviceView& v, const uint16_t* xw, int KW, int64_t M, uint1
   }
 }
 
+struct KsShape {
+  int Q, OB;  // quads of groups per wave, heavy-tailed blocks per wave
+};
+KsShape ks_shape(const DeviceView& v) {
+  const int quads = (v.G + 3) / 4;
+  const int q = (quads + kKsWaves - 1) / kKsWaves;
+  const int nob = (v.n_out + 31) / 32;
+  return KsShape{q < 1 ? 1 : q, (nob + kKsWaves - 1) / kKsWaves};
+}
+
+template <int Q, int OB>
+hipError_t launch_ks_q(const DeviceView& v, const uint16_t* xw, int KW, int64_t M, uint16_t* y, hipStream_t s) {
+  const size_t lds = ks_lds_bytes(KW, M, Q);
+  if (lds > 64 * 1024) {  // dynamic LDS past 64 KiB must be allowed per kernel
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mfma_ks<Q, OB>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t tiles = (v.N + 15) / 16;
+  const int64_t cu = v.cu_count > 0 ? v.cu_count : 1;
+  const unsigned blocks = (unsigned)(tiles < cu ? tiles : cu);
+  hipLaunchKernelGGL((k_mfma_ks<Q, OB>), dim3(blocks), dim3(kKsThreads), lds, s, v, xw, KW, (int)M, y);
+  return hipGetLastError();
+}
+
+template <int OB>
+hipError_t launch_ks_ob(int Q, const DeviceView& v, const uint16_t* xw, int KW, int64_t M, uint16_t* y,
+                        hipStream_t s) {
+  switch (Q) {
+    case 1: return launch_ks_q<1, OB>(v, xw, KW, M, y, s);
+    case 2: return launch_ks_q<2, OB>(v, xw, KW, M, y, s);
+    case 3: return launch_ks_q<3, OB>(v, xw, KW, M, y, s);
+    case 4: return launch_ks_q<4, OB>(v, xw, KW, M, y, s);
+    case 5: return launch_ks_q<5, OB>(v, xw, KW, M, y, s);
+    case 6: return launch_ks_q<6, OB>(v, xw, KW, M, y, s);
+    case 7: return launch_ks_q<7, OB>(v, xw, KW, M, y, s);
+    case 8: return launch_ks_q<8, OB>(v, xw, KW, M, y, s);
+    case 9: return launch_ks_q<9, OB>(v, xw, KW, M, y, s);
+    case 10: return launch_ks_q<10, OB>(v, xw, KW, M, y, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+size_t ks_lds_limit(const DeviceView& v) {
+  const size_t dev = v.lds_per_block > 0 ? (size_t)v.lds_per_block : 64 * 1024;
+  return dev < (size_t)160 * 1024 ? dev : (size_t)160 * 1024;
+}
+
+// The tiled kernel runs 1 <= M <= 16 when the M rows of x, the partial sums
+// and the metadata rows fit in LDS and two tiles fit in registers without
+// spills: Q + OB <= 10 (G <= 320 with no heavy-tailed columns; each further
+// heavy-tailed block per wave takes the place of one quad).
+bool ks_supports(const DeviceView& v, int KW, int64_t M) {
+  if (M < 1 || M > 16) return false;
+  const KsShape sh = ks_shape(v);
+  if (sh.Q > kKsMaxQ || sh.OB > 2 || sh.Q + sh.OB > kKsMaxQ) return false;  // past these: register spills
+  if ((int64_t)M * KW * 2 >= 0x7FFFFFFF || (int64_t)M * (KW / 8) > (int64_t)kKsXSeg * kKsThreads) return false;
+  return ks_lds_bytes(KW, M, sh.Q) <= ks_lds_limit(v);
+}
+
+hipError_t launch_ks(const DeviceView& v, const uint16_t* xw, int KW, int64_t M, uint16_t* y, hipStream_t s) {
+  const KsShape sh = ks_shape(v);
+  switch (sh.OB) {
+    case 0: return launch_ks_ob<0>(sh.Q, v, xw, KW, M, y, s);
+    case 1: return launch_ks_ob<1>(sh.Q, v, xw, KW, M, y, s);
+    default: return launch_ks_ob<2>(sh.Q, v, xw, KW, M, y, s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_mfma_ws(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M,
@@ -355,6 +674,7 @@ hipError_t launch_mfma_ws(const DeviceView& v, const uint16_t* x, uint16_t* y, i
   const unsigned gy = (unsigned)(M < 65535 ? M : 65535);
   hipLaunchKernelGGL(k_xbulk, dim3((unsigned)((KW + kThreads - 1) / kThreads), gy),
                      dim3(kThreads), 0, s, v, x, M, xw, KW);
+  if (ks_supports(v, KW, M)) return launch_ks(v, xw, KW, M, y, s);
   if (M <= 16) launch_mt<1>(v, xw, KW, M, y, s);
   else if (M <= 32) launch_mt<2>(v, xw, KW, M, y, s);
   else if (M <= 64) launch_mt<4>(v, xw, KW, M, y, s);

@@ -375,6 +375,10 @@ MFMA_CASES = [  # (N, K, planted heavy-tailed channels, seed, M)
     (64, 200, 9, 31, 2), (100, 1000, 10, 32, 3), (129, 2088, 40, 33, 16), (300, 96, 3, 34, 17),
     (65, 4096, 40, 35, 33), (257, 2560, 30, 36, 70), (128, 8192, 82, 37, 128), (77, 512, 0, 38, 130),
     (33, 31, 1, 39, 5), (9, 5, 0, 40, 7),
+    # the tiled kernel: ragged tiles, G not a multiple of 4, two heavy-tailed blocks per wave, M = 1
+    (1000, 4000, 300, 43, 8), (45, 1100, 12, 44, 6), (530, 2500, 25, 45, 1), (200, 9728, 150, 46, 7),
+    # beyond its LDS and register limits: the per-wave kernel at small M
+    (300, 12000, 100, 47, 9), (70, 8192, 82, 48, 12),
 ]
 
 
