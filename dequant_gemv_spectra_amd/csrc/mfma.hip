@@ -9,7 +9,10 @@
 // bulk order, zero padded to 32G, followed by the heavy-tailed x values
 // zero padded to a multiple of 32.
 //
-// Pass 2 (k_mfma): a wave owns 16 * NT consecutive output rows for the whole
+// Pass 2 is k_mfma_ks (below) when 1 <= M <= 16 and the M rows of x fit in
+// LDS, else k_mfma.
+//
+// k_mfma: a wave owns 16 * NT consecutive output rows for the whole
 // K loop.  Per chunk of CG groups it loads its code records row-contiguously
 // (consecutive lanes on consecutive records of a row: whole cache lines),
 // stores them to a small wave-private LDS tile and reads them back in the

@@ -122,7 +122,9 @@ typedef enum {
   SPECTRA_KERNEL_AUTO = 0,     /* GEMV for M <= 4 where it supports the shape, MFMA otherwise */
   SPECTRA_KERNEL_GEMV = 1,     /* VALU dequant-GEMV, x in LDS, fp32 accumulate; M <= 4, and
                                   K % 8 == 0 when M > 1 (else SPECTRA_E_UNSUPPORTED) */
-  SPECTRA_KERNEL_MFMA = 2      /* register-dequantized (q - z) tiles on v_mfma_f32_16x16x32_f16 */
+  SPECTRA_KERNEL_MFMA = 2      /* register-dequantized (q - z) tiles on v_mfma_f32_16x16x32_f16:
+                                  16-row tiles with K split over 8 waves when M <= 16 and the M rows
+                                  of x fit in LDS, one 16-row strip per wave otherwise */
 } spectra_kernel;
 
 typedef struct {
