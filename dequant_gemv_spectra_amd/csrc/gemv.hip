@@ -484,6 +484,15 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
   // let the compiler wait for exactly the current tile, so the next one
   // stays in flight.
   if constexpr (NT >= 1) {
+    // several tiles: this lane's groups of x are read from LDS once
+    constexpr bool XR = MX == 1 && P <= 5 && NT >= 2;
+    if constexpr (XR) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int g = lt + L * p;
+        read_x(xs + (g < G ? g : 0) * kXSlot, xreg[p]);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       Frag<P, U, OS>& cur = (t & 1) ? fb : fa;
@@ -491,8 +500,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
       if (t + 1 < NT) load_frag<L, P, U, OS>(nxt, v, row + (t + 1) * stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
       if (row + t * stride < end)
-        compute_frag<L, P, U, OS, MX, false>(cur, v, row + t * stride, end, lt, team, xs, xstride, xor_, tasks.m_rows,
-                                             task.y, nb, xreg);
+        compute_frag<L, P, U, OS, MX, XR>(cur, v, row + t * stride, end, lt, team, xs, xstride, xor_, tasks.m_rows,
+                                          task.y, nb, xreg);
     }
   } else {
     // One row of x: this lane's groups of x stay in registers across the
