@@ -310,10 +310,10 @@ def run_kv(args, sp, torch):
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
            "data": "synthetic",
            "config": {"workload": f"kv-attend-{H * rep_}q-{H}kv-{D}d-{L}ctx", "bytes_per_step": int(step_bytes),
-                      "launches_per_step": 3, "hip_graph": True, "parallelism": "single GPU"},
+                      "launches_per_step": 2, "hip_graph": True, "parallelism": "single GPU"},
            "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
-                        "kernel": "k_kv_scores + k_kv_pv + k_kv_combine", "avg_launch_us": round(ms * 1e3, 3),
+                        "kernel": "k_kv_split + k_kv_combine", "avg_launch_us": round(ms * 1e3, 3),
                         "bytes_per_launch": int(step_bytes)},
            "cpu_baseline": None}
     print(json.dumps(out), flush=True)
