@@ -309,6 +309,56 @@ def test_grouped_launch_matches_single_launches():
         check_product(c, img, x)
 
 
+def test_grouped_launch_chunks_and_mixed_lengths():
+    """Ten containers (more than one launch holds: two launches of 8 and 2) with
+    one long enough for the grid-strided loop next to short ones: every output
+    equals the container's own launch bit for bit."""
+    sp, torch = _sp(), _torch()
+    from dequant_gemv_spectra_amd import synth as S
+    shapes = [(20000, 40), (64, 3), (300, 10), (1, 0), (4097, 20), (17, 2), (1500, 15), (128, 5), (999, 9), (31, 1)]
+    cs, imgs = [], []
+    for i, (N, n_out) in enumerate(shapes):
+        W, g, _ = S.random_case(N, 1024, n_out, 70 + i)
+        c, img = check_pack(W, g)
+        cs.append(c)
+        imgs.append(img)
+    x = np.random.default_rng(9).standard_normal((1, 1024)).astype(np.float16)
+    xs = torch.from_numpy(x).cuda()
+    ys = sp.spectra_gemm_grouped(cs, xs)
+    for c, img, yg in zip(cs, imgs, ys):
+        y1 = sp.spectra_gemm(c, xs, kernel="gemv")
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y1)
+    check_product(cs[0], imgs[0], x, rows=np.arange(0, 20000, 7))
+
+
+def test_two_streams_share_a_container():
+    """One container used at once from two streams (the GEMV at M = 1 on one,
+    the MFMA path with its per-stream workspace at M = 8 on the other): each
+    stream's results equal the same calls made one after another."""
+    sp, torch = _sp(), _torch()
+    from dequant_gemv_spectra_amd import synth as S
+    W, g, _ = S.random_case(3000, 4096, 40, 80)
+    c, img = check_pack(W, g)
+    rng = np.random.default_rng(10)
+    x1 = torch.from_numpy(rng.standard_normal((1, 4096)).astype(np.float16)).cuda()
+    x8 = torch.from_numpy(rng.standard_normal((8, 4096)).astype(np.float16)).cuda()
+    ref1 = sp.spectra_gemm(c, x1)
+    ref8 = sp.spectra_gemm(c, x8)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    out1 = [torch.empty_like(ref1) for _ in range(20)]
+    out8 = [torch.empty_like(ref8) for _ in range(20)]
+    torch.cuda.synchronize()
+    for i in range(20):
+        sp.spectra_gemm(c, x1, out1[i], stream=s1)
+        sp.spectra_gemm(c, x8, out8[i], stream=s2)
+    torch.cuda.synchronize()
+    for i in range(20):
+        assert torch.equal(out1[i], ref1) and torch.equal(out8[i], ref8), i
+    check_product(c, img, x8.cpu().numpy())
+
+
 GEMV_BATCH = [  # (N, K, planted heavy-tailed channels, seed, M): the GEMV with 2 or 4 rows of x
     (64, 2048, 20, 51, 2),    # one slot per lane
     (100, 4096, 40, 52, 3),   # M = 3 in a 4-row batch tile (the fourth row reads zeros)
