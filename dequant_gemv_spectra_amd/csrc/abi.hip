@@ -533,7 +533,10 @@ int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t 
   uint16_t* yp = static_cast<uint16_t*>(y);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (kernel == SPECTRA_KERNEL_GEMV || (kernel == SPECTRA_KERNEL_AUTO && gemv_supports(v, M))) {
+  // auto: the GEMV for M <= 2, and for M = 3, 4 where the tiled MFMA kernel
+  // declines the shape (measured: the tiled kernel is faster from M = 3 on)
+  const bool auto_gemv = gemv_supports(v, M) && (M <= 2 || !mfma_tiled_supports(v, M));
+  if (kernel == SPECTRA_KERNEL_GEMV || (kernel == SPECTRA_KERNEL_AUTO && auto_gemv)) {
     if (!gemv_supports(v, M)) return fail(SPECTRA_E_UNSUPPORTED, "GEMV kernel cannot run this shape");
     e = launch_gemv(v, xp, yp, M, s);
   } else {

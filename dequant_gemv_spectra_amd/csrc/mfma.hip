@@ -467,6 +467,11 @@ __global__ __launch_bounds__(kKsThreads) void k_mfma_ks(const DeviceView v, cons
   __syncthreads();
 
   const uint16_t* xa = xs + (c < M ? c : M - 1) * RS + 8 * r4;  // this lane's A row (rows past M: not stored)
+  // Straight-line compute (no exit past the last group: groups past G load
+  // zero codes, zeros and scales and add exactly 0) lets the scheduler overlap
+  // one quad's loads and products with the next quad's; it takes more
+  // registers, so it is used where it still fits without spills.
+  constexpr bool kFlat = OB == 0 ? Q <= 5 : (OB == 1 ? Q <= 8 : Q <= 6);
   auto compute = [&](const KsFrag<Q, OB>& f, int64_t t) {
     float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
     const uint32_t rowpar = (uint32_t)(((t * 16 + c) * (int64_t)G) & 1);  // flat index parity at group 0
@@ -481,7 +486,8 @@ __global__ __launch_bounds__(kKsThreads) void k_mfma_ks(const DeviceView v, cons
 #pragma unroll
     for (int i = 0; i < Q; ++i) {
       const int gq = 4 * (w * Q + i);
-      if (gq >= G) break;  // wave-uniform
+      if constexpr (!kFlat)
+        if (gq >= G) break;  // wave-uniform
       uint32_t R[4] = {f.c[i].x, f.c[i].y, f.c[i].z, f.c[i].w};
       transpose4(R[0], R[1], R[2], R[3]);
       const uint2 s4 = *reinterpret_cast<const uint2*>(ms + c * MS + 4 * i);
@@ -490,16 +496,20 @@ __global__ __launch_bounds__(kKsThreads) void k_mfma_ks(const DeviceView v, cons
       float4_t p[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (gq + j >= G) break;
+        if constexpr (!kFlat)
+          if (gq + j >= G) break;
+        // past G (straight-line form only) any x slot of the row will do
+        const int ga = gq + j < G ? gq + j : (G > 0 ? G - 1 : 0);
         const uint32_t par = (rowpar ^ (uint32_t)(gq + j)) & 1u;
         const uint32_t z = (z4 >> (8u * j + 4u * par)) & 0xFu;
         const half8 b = dequant_word(R[j], z);
-        const half8 a = *reinterpret_cast<const half8*>(xa + 32 * (gq + j));
+        const half8 a = *reinterpret_cast<const half8*>(xa + 32 * ga);
         p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (gq + j >= G) break;
+        if constexpr (!kFlat)
+          if (gq + j >= G) break;
         acc += h2f((uint16_t)S[j]) * p[j];
       }
     }
@@ -669,6 +679,10 @@ hipError_t launch_ks(const DeviceView& v, const uint16_t* xw, int KW, int64_t M,
 }
 
 }  // namespace
+
+bool mfma_tiled_supports(const DeviceView& v, int64_t M) {
+  return ks_supports(v, 32 * v.G + ((v.n_out + 31) & ~31), M);
+}
 
 hipError_t launch_mfma_ws(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M,
                           void* workspace, hipStream_t s) {

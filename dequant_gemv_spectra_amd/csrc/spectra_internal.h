@@ -111,6 +111,8 @@ hipError_t launch_gemv(const DeviceView& v, const uint16_t* x, uint16_t* y, int6
 hipError_t launch_gemv_grouped(const DeviceView* vs, int count, const uint16_t* x,
                                uint16_t* const* ys, hipStream_t s);
 bool mfma_supports(const DeviceView& v, int64_t M);
+// The MFMA path runs the shape on its 16-row tiled kernel (k_mfma_ks).
+bool mfma_tiled_supports(const DeviceView& v, int64_t M);
 // Device workspace the MFMA path needs for M input rows (x permuted to bulk order).
 size_t mfma_workspace_bytes(const DeviceView& v, int64_t M);
 hipError_t launch_mfma_ws(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M,

@@ -119,7 +119,8 @@ typedef enum {
 
 /* Kernel selection for spectra_gemm_ex. */
 typedef enum {
-  SPECTRA_KERNEL_AUTO = 0,     /* GEMV for M <= 4 where it supports the shape, MFMA otherwise */
+  SPECTRA_KERNEL_AUTO = 0,     /* GEMV for M <= 2 (M <= 4 where the tiled MFMA kernel declines the
+                                  shape) if it supports the shape, MFMA otherwise */
   SPECTRA_KERNEL_GEMV = 1,     /* VALU dequant-GEMV, x in LDS, fp32 accumulate; M <= 4, and
                                   K % 8 == 0 when M > 1 (else SPECTRA_E_UNSUPPORTED) */
   SPECTRA_KERNEL_MFMA = 2      /* register-dequantized (q - z) tiles on v_mfma_f32_16x16x32_f16:

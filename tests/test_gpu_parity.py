@@ -374,7 +374,7 @@ def test_gemv_batch_rows(N, K, n_out, seed, M):
     W, g, x = synth.random_case(N, K, n_out, seed, M=M)
     c, img = check_pack(W, g)
     check_product(c, img, x, kernel="gemv")
-    check_product(c, img, x)  # auto picks the GEMV for M <= 4
+    check_product(c, img, x)  # auto: the GEMV for M <= 2, the tiled MFMA kernel for M = 3, 4 where it runs
 
 
 def test_gemv_batch_declines():
@@ -475,6 +475,7 @@ def test_config_large_batched(cfg):
         if M == 1:
             continue
         x = synth.activations(lin, cfg, M)
-        check_product(c, img, x, rows=rows)
-        if M <= 4:  # auto ran the GEMV: the MFMA path at the same M too
+        check_product(c, img, x, rows=rows)  # auto
+        if M <= 4:  # both kernels at the same M
+            check_product(c, img, x, rows=rows, kernel="gemv")
             check_product(c, img, x, rows=rows, kernel="mfma")
