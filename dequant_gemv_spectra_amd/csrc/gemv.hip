@@ -25,8 +25,10 @@
 // the gather and its barriers run while that tile is on its way from HBM (a
 // wave's loads complete in issue order: had the tile gone first, the gather
 // would have waited for it).  In LDS each group's 32 halves occupy an 80-byte
-// slot, which keeps the per-lane 16-byte reads free of bank conflicts.  One
-// block of 512 lanes per compute unit keeps the staging to one copy per CU.
+// slot, which keeps the per-lane 16-byte reads free of bank conflicts.  Blocks
+// of 512 lanes, one per compute unit (one staging copy per CU), or two on
+// long launches when registers and LDS allow (one wave's dequantization then
+// overlaps another's loads).
 //
 // Code records are read with the non-temporal hint: each is used once, and
 // the hint keeps them from displacing x, perm and the metadata in the caches.

@@ -1,5 +1,6 @@
 // SPECTRA batched product for gfx950: y = x W_hat^T on the matrix cores
-// (v_mfma_f32_16x16x32_f16), for M >= 5 and the shapes the GEMV declines.
+// (v_mfma_f32_16x16x32_f16): automatic from M = 3 on (the GEMV keeps M <= 2,
+// and M <= 4 where the tiled kernel declines), and for shapes the GEMV declines.
 //
 // The SPECTRA page reports Tensor-Core prefill next to its decode kernels
 // (highlight 4); this is the gfx950 counterpart for batched rows, written for

@@ -436,7 +436,7 @@ MFMA_CASES = [  # (N, K, planted heavy-tailed channels, seed, M)
 def test_mfma_product_small(N, K, n_out, seed, M):
     W, g, x = synth.random_case(N, K, n_out, seed, M=M)
     c, img = check_pack(W, g)
-    check_product(c, img, x)                   # auto: the MFMA path for M >= 5 (and shapes the GEMV declines)
+    check_product(c, img, x)                   # auto: the MFMA path from M = 3 (and shapes the GEMV declines)
     check_product(c, img, x, kernel="mfma")
 
 
