@@ -318,34 +318,57 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
 // split weights are computed once into LDS; each thread then sums its
 // channel over the splits with several loads in flight.
 constexpr int kMaxSplits = 4096;
-__global__ __launch_bounds__(256) void k_kv_combine(const float* __restrict__ part, const float* __restrict__ stats,
-                                                    int splits, int Hq, int D, uint16_t* __restrict__ out) {
+constexpr int kCombThreads = 256;
+constexpr int kCombFirst = 32;  // partials per thread requested with the stats, in one round trip
+// One block per query head hq.  Thread t owns channel d = t % D and the
+// splits sp = t / D (mod R), R = 256 / D threads per channel.  The stats of
+// every split and the thread's first kCombFirst partials are requested
+// together (the partials do not depend on the weights), so a call over up to
+// R * kCombFirst splits waits for one round of loads: global max, weights
+// exp(m - M) in LDS, sum of weights times exp sums, weighted partial sums,
+// the R threads of a channel added in LDS, divided, fp16.
+__global__ __launch_bounds__(kCombThreads) void k_kv_combine(const float* __restrict__ part,
+                                                            const float* __restrict__ stats, int splits, int Hq,
+                                                            int D, uint16_t* __restrict__ out) {
   __shared__ float wgt[kMaxSplits];
-  __shared__ float red[4];
-  const int hq = blockIdx.x;
-  float M = -INFINITY;
-  for (int sp = threadIdx.x; sp < splits; sp += blockDim.x) M = fmaxf(M, stats[2 * ((int64_t)sp * Hq + hq)]);
-  M = block_max(M, red);
-  float l = 0.f;
-  for (int sp = threadIdx.x; sp < splits; sp += blockDim.x) {
-    const int64_t b = (int64_t)sp * Hq + hq;
-    const float w = __expf(stats[2 * b] - M);
-    wgt[sp] = w;
-    l += w * stats[2 * b + 1];
+  __shared__ float osum[kCombThreads];
+  __shared__ float red[kCombThreads / 64];
+  const int hq = blockIdx.x, t = threadIdx.x;
+  const int R = kCombThreads / D, d = t % D, r = t / D;
+  float pv[kCombFirst];
+#pragma unroll
+  for (int i = 0; i < kCombFirst; ++i) {
+    const int sp = r + R * i;
+    pv[i] = sp < splits ? part[((int64_t)sp * Hq + hq) * D + d] : 0.f;
   }
-  l = block_sum(l, red);  // its barriers also publish wgt
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int sp = 0;
-    for (; sp + 8 <= splits; sp += 8) {
-      float v[8];
+  float M = -INFINITY;
+  for (int sp = t; sp < splits; sp += kCombThreads) {
+    const float m = stats[2 * ((int64_t)sp * Hq + hq)];
+    wgt[sp] = m;
+    M = fmaxf(M, m);
+  }
+  M = block_max(M, red);  // its barriers also publish the maxima in wgt
+  float l = 0.f;
+  for (int sp = t; sp < splits; sp += kCombThreads) {
+    const float w = __expf(wgt[sp] - M);
+    wgt[sp] = w;
+    l += w * stats[2 * ((int64_t)sp * Hq + hq) + 1];
+  }
+  l = block_sum(l, red);  // its barriers also publish the weights
+  float o0 = 0.f, o1 = 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = part[((int64_t)(sp + u) * Hq + hq) * D + d];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) o[u] = __builtin_fmaf(wgt[sp + u], v[u], o[u]);
-    }
-    for (; sp < splits; ++sp) o[0] = __builtin_fmaf(wgt[sp], part[((int64_t)sp * Hq + hq) * D + d], o[0]);
-    const float tot = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
+  for (int i = 0; i < kCombFirst; i += 2) {
+    const int sp = r + R * i;
+    if (sp < splits) o0 = __builtin_fmaf(wgt[sp], pv[i], o0);
+    if (sp + R < splits) o1 = __builtin_fmaf(wgt[sp + R], pv[i + 1], o1);
+  }
+  for (int sp = r + R * kCombFirst; sp < splits; sp += R)  // long contexts: the rest
+    o0 = __builtin_fmaf(wgt[sp], part[((int64_t)sp * Hq + hq) * D + d], o0);
+  osum[t] = o0 + o1;
+  __syncthreads();
+  if (r == 0) {
+    float tot = osum[d];
+    for (int rr = 1; rr < R; ++rr) tot += osum[d + rr * D];
     out[(int64_t)hq * D + d] = __builtin_bit_cast(uint16_t, (_Float16)(tot / l));
   }
 }
@@ -367,8 +390,8 @@ hipError_t attend_gr(const KvView& c, const uint16_t* q, int64_t L, uint16_t* ou
   float* stats = part + (size_t)splits * Hq * D;
   hipLaunchKernelGGL((k_kv_split<G, REP>), dim3((unsigned)splits, (unsigned)c.H), dim3(kPvThreads), 0, s, c, q, L,
                      part, stats);
-  hipLaunchKernelGGL(k_kv_combine, dim3((unsigned)Hq), dim3(D < 256 ? D : 256), 0, s, part, stats, (int)splits,
-                     Hq, D, out);
+  hipLaunchKernelGGL(k_kv_combine, dim3((unsigned)Hq), dim3(kCombThreads), 0, s, part, stats, (int)splits, Hq, D,
+                     out);
   return hipGetLastError();
 }
 
