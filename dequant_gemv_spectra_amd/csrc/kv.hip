@@ -139,15 +139,19 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 // One block per (split of kTokensPerSplit tokens, cache head h), serving the
 // rep query heads that read h:
-//   1. the value records of the split are requested first (lane-per-channel-
-//      pair: lane l owns pairs l + 64 i; each wave every WAVES-th token);
+//   1. the value records, scales and zero bytes of the split are requested
+//      first, 16 bytes of records per thread and load (as many small
+//      per-lane loads cost 3 % more); they are stored to LDS once the scores
+//      are done;
 //   2. threads 0 .. 127 take one token each: dequantize its key (exact fp16
 //      (q - z) pairs), dot it with the rep queries in fp32, times s16 per
 //      group, over sqrt(D) -> scores in LDS;
 //   3. per query head the split's max m and l = sum exp(s - m); the scores
 //      become p = exp(s - m);
-//   4. sum_t p_t v_t per query head in registers, reduced across the waves
-//      -> fp32 partials and (m, l) per (split, query head).
+//   4. sum_t p_t v_t per query head in registers (lane-per-channel-pair:
+//      lane l owns pairs l + 64 i, each wave every WAVES-th token, values
+//      dequantized from LDS), reduced across the waves -> fp32 partials and
+//      (m, l) per (split, query head).
 // The keys and values of the split are read once for all rep query heads.
 template <int G, int REP>
 __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const uint16_t* __restrict__ q,
@@ -160,8 +164,7 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
   constexpr int WAVES = kPvThreads / 64;
   constexpr int TS = kTokensPerSplit;
   constexpr int UN = TS / WAVES;              // tokens per wave
-  constexpr int STEPS = PL;                   // value loads in STEPS rounds of UNS tokens
-  constexpr int UNS = UN / STEPS;
+  constexpr int RPT = TS * G / kPvThreads;    // value records per thread
   __shared__ half2_t qs[REP][D / 2];
   __shared__ float sc[REP][TS];
   __shared__ float mst[REP], lst[REP];
@@ -175,25 +178,22 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
     qs[rr][j] = as_h2(reinterpret_cast<const uint32_t*>(q + (int64_t)(h * rep + rr) * D)[j]);
   }
 
-  // 1. value loads of this wave's first UNS tokens (tokens past L read token t0's)
-  uint32_t vw[UNS][PL], vz[UNS][PL];
-  uint16_t vs[UNS][PL];
-  auto load_v = [&](int step) {
+  // 1. the split's value records, scales and zero bytes, a few wide loads per
+  //    thread (tokens past L read token t0's); they go to LDS after the scores
+  __shared__ u32x4 vrec[TS * G];
+  __shared__ uint16_t vscl[TS * G];
+  __shared__ uint8_t vzb[TS * G / 2];
+  u32x4 vr[RPT];
+  uint32_t vsr[RPT], vzr[RPT];
 #pragma unroll
-    for (int u = 0; u < UNS; ++u) {
-      const int64_t t = t0 + wave + (int64_t)WAVES * (step * UNS + u);
-      const int64_t flat0 = ((t < L ? t : t0) * H + h) * G;
-#pragma unroll
-      for (int i = 0; i < PL; ++i) {
-        const int pi = (lane + 64 * i) % NP;  // lanes past NP (D = 64) read a valid pair, unused
-        const int g = pi >> 4, e = (2 * pi) & 31;
-        vw[u][i] = reinterpret_cast<const uint32_t*>(c.v.codes + flat0 + g)[e >> 3];
-        vs[u][i] = c.v.scales[flat0 + g];
-        vz[u][i] = c.v.zeros[(flat0 + g) >> 1];
-      }
-    }
-  };
-  load_v(0);
+  for (int i = 0; i < RPT; ++i) {
+    const int idx = threadIdx.x + kPvThreads * i, tl = idx / G, g = idx % G;
+    const int64_t t = t0 + tl;
+    const int64_t flat = ((t < L ? t : t0) * H + h) * G + g;
+    vr[i] = *reinterpret_cast<const u32x4*>(c.v.codes + flat);
+    vsr[i] = c.v.scales[flat];
+    vzr[i] = c.v.zeros[flat >> 1];  // the byte of groups g, g + 1 (flat and g have the same parity)
+  }
   __syncthreads();  // qs ready
 
   // 2. scores: every key load of the token first, then the arithmetic
@@ -239,6 +239,13 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
 #pragma unroll
     for (int rr = 0; rr < REP; ++rr) sc[rr][tl] = t < L ? acc[rr] * inv_sqrt_d : -INFINITY;
   }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int idx = threadIdx.x + kPvThreads * i;
+    vrec[idx] = vr[i];
+    vscl[idx] = (uint16_t)vsr[i];
+    if ((idx & 1) == 0) vzb[idx >> 1] = (uint8_t)vzr[i];
+  }
   __syncthreads();
 
   // 3. split max and exp sums, one query head per wave at a time
@@ -266,26 +273,24 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
   for (int rr = 0; rr < REP; ++rr)
 #pragma unroll
     for (int i = 0; i < PL; ++i) a[rr][i][0] = a[rr][i][1] = 0.f;
+#pragma unroll 4
+  for (int u = 0; u < UN; ++u) {
+    const int tl = wave + WAVES * u;
 #pragma unroll
-  for (int step = 0; step < STEPS; ++step) {
-    if (step) load_v(step);
+    for (int i = 0; i < PL; ++i) {
+      const int pi = (lane + 64 * i) % NP;  // lanes past NP (D = 64) take a valid pair, unused
+      const int g = pi >> 4, e = (2 * pi) & 31;
+      const int idx = tl * G + g;
+      const uint32_t w = reinterpret_cast<const uint32_t*>(vrec)[4 * idx + (e >> 3)];
+      const uint32_t z = ((uint32_t)vzb[idx >> 1] >> (4 * (g & 1))) & 0xFu;
+      const half2_t qz = pair_qz(w, (e & 7) >> 1, z);
+      const float s16 = h2f(vscl[idx]);
+      const float v0 = (float)qz.x * s16, v1 = (float)qz.y * s16;
 #pragma unroll
-    for (int u = 0; u < UNS; ++u) {
-      const int tl = wave + WAVES * (step * UNS + u);
-#pragma unroll
-      for (int i = 0; i < PL; ++i) {
-        const int pi = (lane + 64 * i) % NP;
-        const int g = pi >> 4, e = (2 * pi) & 31;
-        const uint32_t z = (vz[u][i] >> (4 * (g & 1))) & 0xFu;
-        const half2_t qz = pair_qz(vw[u][i], (e & 7) >> 1, z);
-        const float s16 = h2f(vs[u][i]);
-        const float v0 = (float)qz.x * s16, v1 = (float)qz.y * s16;
-#pragma unroll
-        for (int rr = 0; rr < REP; ++rr) {
-          const float p = sc[rr][tl];
-          a[rr][i][0] = __builtin_fmaf(p, v0, a[rr][i][0]);
-          a[rr][i][1] = __builtin_fmaf(p, v1, a[rr][i][1]);
-        }
+      for (int rr = 0; rr < REP; ++rr) {
+        const float p = sc[rr][tl];
+        a[rr][i][0] = __builtin_fmaf(p, v0, a[rr][i][0]);
+        a[rr][i][1] = __builtin_fmaf(p, v1, a[rr][i][1]);
       }
     }
   }
