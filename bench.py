@@ -111,15 +111,18 @@ def grouped_call(sp, ps):
 
 
 def layer_units(sp, packed, M, kern, tag):
-    """Launch units of one decoder layer: (label, kind, callable, bytes)."""
+    """Launch units of one decoder layer: (label, kind, callable, bytes, kernel run)."""
     by = {p.lin.name.split(".")[-1]: p for p in packed}
+    plan = lambda p: sp.spectra_gemm_plan(p.c, M, kern)
     if M == 1 and kern in ("auto", "gemv"):
         qkv, gu = [by["q"], by["k"], by["v"]], [by["gate"], by["up"]]
-        return [(f"{tag}.qkv", "qkv", grouped_call(sp, qkv), sum(p.bytes for p in qkv) - 2 * 2 * by["q"].lin.K),
-                (f"{tag}.o", "o", gemm_call(sp, by["o"], kern), by["o"].bytes),
-                (f"{tag}.gate_up", "gate_up", grouped_call(sp, gu), sum(p.bytes for p in gu) - 2 * by["gate"].lin.K),
-                (f"{tag}.down", "down", gemm_call(sp, by["down"], kern), by["down"].bytes)]
-    return [(f"{tag}.{nm}", nm, gemm_call(sp, by[nm], kern), by[nm].bytes)
+        return [(f"{tag}.qkv", "qkv", grouped_call(sp, qkv), sum(p.bytes for p in qkv) - 2 * 2 * by["q"].lin.K,
+                 "k_gemv_m1"),
+                (f"{tag}.o", "o", gemm_call(sp, by["o"], kern), by["o"].bytes, plan(by["o"])),
+                (f"{tag}.gate_up", "gate_up", grouped_call(sp, gu), sum(p.bytes for p in gu) - 2 * by["gate"].lin.K,
+                 "k_gemv_m1"),
+                (f"{tag}.down", "down", gemm_call(sp, by["down"], kern), by["down"].bytes, plan(by["down"]))]
+    return [(f"{tag}.{nm}", nm, gemm_call(sp, by[nm], kern), by[nm].bytes, plan(by[nm]))
             for nm in ("q", "k", "v", "o", "gate", "up", "down")]
 
 
@@ -157,7 +160,8 @@ def build_units(args, sp, torch):
     copies = max(1, int(args.rotate_gib * 2 ** 30 // first.bytes) + 1)
     packed = [first] + [Linear(sp, torch, lin, cfg, M, W, g, copy=cp) for cp in range(1, copies)]
     log(f"{wl.name}: {copies} distinct copies, {first.bytes / 1e6:.1f} MB each")
-    units = [(f"{lin.name}#{i}", lin.name, gemm_call(sp, p, kern), p.bytes) for i, p in enumerate(packed)]
+    units = [(f"{lin.name}#{i}", lin.name, gemm_call(sp, p, kern), p.bytes, sp.spectra_gemm_plan(p.c, M, kern))
+             for i, p in enumerate(packed)]
     return wl.name, units, False
 
 
@@ -444,15 +448,17 @@ def main():
 
     # roofline of the dominant kernel kind
     kinds = {}
-    for _, kind, f, b in units:
-        kinds.setdefault(kind, []).append((f, b))
-    dom = max(kinds, key=lambda k: sum(b for _, b in kinds[k]))
-    dgraph = capture(torch, [f for f, _ in kinds[dom]])
+    for _, kind, f, b, plan in units:
+        kinds.setdefault(kind, []).append((f, b, plan))
+    dom = max(kinds, key=lambda k: sum(b for _, b, _ in kinds[k]))
+    dgraph = capture(torch, [f for f, _, _ in kinds[dom]])
     dgraph.replay()
     dms = time_graph(torch, dgraph, 10) / len(kinds[dom])
-    dbytes = sum(b for _, b in kinds[dom]) / len(kinds[dom])
+    dbytes = sum(b for _, b, _ in kinds[dom]) / len(kinds[dom])
     achieved = dbytes / (dms * 1e-3) / 1e9
-    kernel_name = "k_gemv_m1" if (args.M == 1 and args.kernel != "mfma") else "k_mfma"
+    kernel_name = kinds[dom][0][2]  # as the library reports it (spectra_gemm_plan)
+    if kernel_name != "k_gemv_m1":
+        kernel_name = "k_xbulk + " + kernel_name
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                 "kernel": f"{kernel_name} ({dom} launches)", "avg_launch_us": round(dms * 1e3, 3),

@@ -519,28 +519,56 @@ int spectra_export(const spectra_container* c, void* host_dst, uint64_t cap) {
   return SPECTRA_OK;
 }
 
+namespace {
+
+// The kernel a product of M rows runs with the selector, or a status < 0
+// (message set).  The container must be live and M and kernel in range.
+int plan_of(const DeviceView& v, int64_t M, int kernel) {
+  // auto: the GEMV for M <= 2, and for M = 3, 4 where the tiled MFMA kernel
+  // declines the shape (measured: the tiled kernel is faster from M = 3 on)
+  const bool auto_gemv = gemv_supports(v, M) && (M <= 2 || !mfma_tiled_supports(v, M));
+  if (kernel == SPECTRA_KERNEL_GEMV || (kernel == SPECTRA_KERNEL_AUTO && auto_gemv)) {
+    if (!gemv_supports(v, M)) return fail(SPECTRA_E_UNSUPPORTED, "GEMV kernel cannot run this shape");
+    return SPECTRA_PLAN_GEMV;
+  }
+  if (!mfma_supports(v, M)) return fail(SPECTRA_E_UNSUPPORTED, "MFMA kernel cannot run this shape");
+  return mfma_tiled_supports(v, M) ? SPECTRA_PLAN_MFMA_TILED : SPECTRA_PLAN_MFMA;
+}
+
+int check_gemm_args(const spectra_container* c, int64_t M, int kernel) {
+  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+  if (M < 1 || M > SPECTRA_MAX_M) return fail(SPECTRA_E_INVAL, "M out of range [1, 2^20]");
+  if (kernel < SPECTRA_KERNEL_AUTO || kernel > SPECTRA_KERNEL_MFMA)
+    return fail(SPECTRA_E_INVAL, "unknown kernel selector");
+  return SPECTRA_OK;
+}
+
+}  // namespace
+
+int spectra_gemm_plan(const spectra_container* c, int64_t M, int kernel) {
+  const int st = check_gemm_args(c, M, kernel);
+  if (st != SPECTRA_OK) return st;
+  return plan_of(c->view(), M, kernel);
+}
+
 int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t M, void* stream,
                     int kernel) {
   if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
   if (!x || !y) return fail(SPECTRA_E_INVAL, "null x or y");
   if ((reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(y) & 3))
     return fail(SPECTRA_E_INVAL, "x and y must be 4-byte aligned");
-  if (M < 1 || M > SPECTRA_MAX_M) return fail(SPECTRA_E_INVAL, "M out of range [1, 2^20]");
-  if (kernel < SPECTRA_KERNEL_AUTO || kernel > SPECTRA_KERNEL_MFMA)
-    return fail(SPECTRA_E_INVAL, "unknown kernel selector");
+  const int st = check_gemm_args(c, M, kernel);
+  if (st != SPECTRA_OK) return st;
   const DeviceView v = c->view();
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   uint16_t* yp = static_cast<uint16_t*>(y);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  // auto: the GEMV for M <= 2, and for M = 3, 4 where the tiled MFMA kernel
-  // declines the shape (measured: the tiled kernel is faster from M = 3 on)
-  const bool auto_gemv = gemv_supports(v, M) && (M <= 2 || !mfma_tiled_supports(v, M));
-  if (kernel == SPECTRA_KERNEL_GEMV || (kernel == SPECTRA_KERNEL_AUTO && auto_gemv)) {
-    if (!gemv_supports(v, M)) return fail(SPECTRA_E_UNSUPPORTED, "GEMV kernel cannot run this shape");
+  const int plan = plan_of(v, M, kernel);
+  if (plan < 0) return plan;
+  if (plan == SPECTRA_PLAN_GEMV) {
     e = launch_gemv(v, xp, yp, M, s);
   } else {
-    if (!mfma_supports(v, M)) return fail(SPECTRA_E_UNSUPPORTED, "MFMA kernel cannot run this shape");
     void* ws = nullptr;
     e = stream_workspace(c->device, s, mfma_workspace_bytes(v, M), &ws);
     if (e != hipSuccess) return fail(SPECTRA_E_NOMEM, hip_msg("MFMA workspace", e));

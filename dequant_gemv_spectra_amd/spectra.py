@@ -24,7 +24,7 @@ SPECTRA_E_IO = -6
 
 KERNELS = {"auto": 0, "gemv": 1, "mfma": 2}
 
-EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm_ex",
+EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm_ex", "spectra_gemm_plan",
             "spectra_gemm_grouped", "spectra_embed", "spectra_free", "spectra_info",
             "spectra_export", "spectra_validate_image", "spectra_import", "spectra_save",
             "spectra_load", "spectra_kv_create", "spectra_kv_append", "spectra_kv_attend",
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.spectra_gemm.restype = c_int
     L.spectra_gemm_ex.argtypes = [vp, vp, vp, i64, vp, c_int]
     L.spectra_gemm_ex.restype = c_int
+    L.spectra_gemm_plan.argtypes = [vp, i64, c_int]
+    L.spectra_gemm_plan.restype = c_int
     L.spectra_gemm_grouped.argtypes = [ctypes.POINTER(vp), c_int, vp, ctypes.POINTER(vp), i64, vp]
     L.spectra_gemm_grouped.restype = c_int
     L.spectra_embed.argtypes = [vp, vp, i64, vp, vp]
@@ -207,6 +209,17 @@ def spectra_gemm(c: Container, x, y=None, stream=None, kernel: str = "auto"):
     _check(lib().spectra_gemm_ex(c.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
                                  M, _stream_ptr(stream), KERNELS[kernel]))
     return y
+
+
+PLANS = {1: "k_gemv_m1", 2: "k_mfma_ks", 3: "k_mfma"}
+
+
+def spectra_gemm_plan(c: Container, M: int, kernel: str = "auto") -> str:
+    """Name of the kernel spectra_gemm would run for M rows of x (no device work)."""
+    st = lib().spectra_gemm_plan(c.handle, M, KERNELS[kernel])
+    if st < 0:
+        _check(st)
+    return PLANS[st]
 
 
 def spectra_gemm_grouped(cs, x, ys=None, stream=None):

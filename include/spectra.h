@@ -172,6 +172,19 @@ int spectra_gemm(const spectra_container* c, const void* x, void* y, int64_t M);
 int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t M,
                     void* stream, int kernel);
 
+/* Which kernel spectra_gemm_ex would run for M rows of x and the selector
+ * `kernel` (a spectra_kernel), without any device work.  Returns
+ * SPECTRA_PLAN_GEMV, SPECTRA_PLAN_MFMA_TILED or SPECTRA_PLAN_MFMA; or, as
+ * spectra_gemm_ex would, SPECTRA_E_INVAL (invalid container, M out of range,
+ * unknown selector) or SPECTRA_E_UNSUPPORTED (a forced kernel that cannot run
+ * the shape). */
+enum {
+  SPECTRA_PLAN_GEMV = 1,        /* k_gemv_m1: VALU dequant-GEMV */
+  SPECTRA_PLAN_MFMA_TILED = 2,  /* k_xbulk + k_mfma_ks: 16-row tiles, K split over 8 waves */
+  SPECTRA_PLAN_MFMA = 3         /* k_xbulk + k_mfma: one 16-row strip per wave */
+};
+int spectra_gemm_plan(const spectra_container* c, int64_t M, int kernel);
+
 /* Several containers that share K and the same input x (e.g. the q/k/v or the
  * gate/up projections of one decoder layer) in one launch: ys[i] = x W_i^T.
  * cs and ys are HOST arrays of `count` entries (1 <= count <= 64); every ys[i]

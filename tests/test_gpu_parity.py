@@ -332,6 +332,34 @@ def test_grouped_launch_chunks_and_mixed_lengths():
     check_product(cs[0], imgs[0], x, rows=np.arange(0, 20000, 7))
 
 
+def test_kernel_plan_follows_the_selection_rule():
+    """spectra_gemm_plan names what spectra_gemm_ex runs: the GEMV up to M = 2,
+    the tiled MFMA kernel from M = 3 where it runs the shape, the GEMV again at
+    M = 3, 4 where it does not (here: more than 16 heavy-tailed blocks), and
+    k_mfma past both (here: more groups per row than either holds)."""
+    sp = _sp()
+    from dequant_gemv_spectra_amd import synth as S
+    W, g, _ = S.random_case(100, 4096, 40, 90)
+    c4k, _ = check_pack(W, g)
+    W, g, _ = S.random_case(2048, 2520, 600, 91)  # G = 60: one slot per 64-lane team, so the GEMV takes M = 4
+    cout, img = check_pack(W, g)
+    assert O.unpack(img)["n_out"] > 16 * 32
+    W, g, _ = S.random_case(40, 15000, 100, 92)
+    c15k, _ = check_pack(W, g)
+    assert [sp.spectra_gemm_plan(c4k, M) for M in (1, 2, 3, 4, 8, 16, 17)] == \
+        ["k_gemv_m1"] * 2 + ["k_mfma_ks"] * 4 + ["k_mfma"]
+    assert [sp.spectra_gemm_plan(cout, M) for M in (1, 2, 3, 4, 5)] == ["k_gemv_m1"] * 4 + ["k_mfma"]
+    assert [sp.spectra_gemm_plan(c15k, M) for M in (1, 2, 3, 5)] == ["k_gemv_m1"] * 2 + ["k_mfma"] * 2
+    assert sp.spectra_gemm_plan(c4k, 3, kernel="gemv") == "k_gemv_m1"
+    assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma") == "k_mfma_ks"
+    with pytest.raises(sp.SpectraError) as ei:
+        sp.spectra_gemm_plan(c4k, 8, kernel="gemv")  # the GEMV takes M <= 4
+    assert ei.value.status == sp.SPECTRA_E_UNSUPPORTED
+    with pytest.raises(sp.SpectraError) as ei:
+        sp.spectra_gemm_plan(c4k, 0)
+    assert ei.value.status == sp.SPECTRA_E_INVAL
+
+
 def test_two_streams_share_a_container():
     """One container used at once from two streams (the GEMV at M = 1 on one,
     the MFMA path with its per-stream workspace at M = 8 on the other): each
