@@ -54,6 +54,9 @@ def test_status_codes_match_header():
         assert getattr(sp, name) == int(val), name
     kernels = dict(re.findall(r"SPECTRA_KERNEL_(\w+)\s*=\s*(\d+)", text))
     assert {k.lower(): int(v) for k, v in kernels.items()} == sp.KERNELS
+    plans = {int(v): k for k, v in re.findall(r"SPECTRA_PLAN_(\w+)\s*=\s*(\d+)", text)}
+    assert plans == {1: "GEMV", 2: "MFMA_TILED", 3: "MFMA"}
+    assert sp.PLANS == {1: "k_gemv_m1", 2: "k_mfma_ks", 3: "k_mfma"}
 
 
 def test_host_argument_checks_without_a_device():
@@ -65,6 +68,8 @@ def test_host_argument_checks_without_a_device():
     assert L.spectra_info(None, ctypes.byref(info)) == sp.SPECTRA_E_INVAL
     assert L.spectra_gemm(None, P(16), P(16), 1) == sp.SPECTRA_E_INVAL
     assert L.spectra_gemm_ex(P(0x1000), P(16), P(16), 1, None, 0) == sp.SPECTRA_E_INVAL  # not a live handle
+    assert L.spectra_gemm_plan(None, 1, 0) == sp.SPECTRA_E_INVAL
+    assert L.spectra_gemm_plan(P(0x1000), 1, 0) == sp.SPECTRA_E_INVAL
     assert L.spectra_export(None, None, 0) == sp.SPECTRA_E_INVAL
     assert L.spectra_gemm_grouped(None, 1, None, None, 1, None) == sp.SPECTRA_E_INVAL
     L.spectra_free(None)
