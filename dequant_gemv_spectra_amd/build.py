@@ -24,7 +24,8 @@ ARCH = "gfx950"
 SOURCES = {
     "abi.hip": [],
     "pack.hip": ["-ffp-contract=off"],
-    "gemv.hip": [],
+    # the kernel's three leading task boundaries land in scalar registers at launch
+    "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=3"],
     "mfma.hip": [],
     "embed.hip": [],
     "kv.hip": ["-ffp-contract=off"],

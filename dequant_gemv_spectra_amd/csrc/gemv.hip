@@ -75,10 +75,12 @@ struct GemvTask {
   int32_t rows_per_block;  // contiguous rows per block (short launches), else 0
 };
 
-// Kernel arguments.  A block finds its task from `begin` alone (one batch of
-// scalar loads, unrolled over every entry) and then reads that task's fields
-// in a second batch: two dependent round trips to the argument memory before
-// its first vector load, each of which costs on the order of 0.5 us.
+// Kernel arguments.  The first blocks of tasks 1 .. 3 also come as three
+// leading scalar arguments, which the build preloads into scalar registers
+// (kernarg preloading, -amdgpu-kernarg-preload-count=3): a block of the first
+// four tasks finds its task with no memory access and then reads that task's
+// fields in one batch of scalar loads, a single round trip to the argument
+// memory before its first vector load.  Tasks 4 .. 7 read `begin` first.
 struct GemvTasks {
   int32_t begin[kMaxTasks];  // first block of each task; INT32_MAX past the last task
   int32_t count;
@@ -423,18 +425,30 @@ __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const Devi
 //
 // MX rows of x (a batch tile, M <= MX) share every dequantized record.
 template <int L, int P, int U, int NT, int MX>
-__global__ __launch_bounds__(kBlock) void k_gemv_m1(const GemvTasks tasks) {
+__global__ __launch_bounds__(kBlock) void k_gemv_m1(const int32_t begin1, const int32_t begin2,
+                                                    const int32_t begin3, const GemvTasks tasks) {
   constexpr int OS = (L == 16) ? 4 : 2;  // heavy-tailed slots per lane held in registers
   constexpr int T = kBlock / L;          // teams per block
   constexpr int kTileRows = T * U;
   extern __shared__ __align__(16) unsigned char smem[];
   int ti = 0, first = 0;  // the block's task and that task's first block
+  const int32_t bx = (int32_t)blockIdx.x;
+  if (bx >= begin3) {
+    ti = 3;
+    first = begin3;
 #pragma unroll
-  for (int i = 1; i < kMaxTasks; ++i)
-    if ((int32_t)blockIdx.x >= tasks.begin[i]) {
-      ti = i;
-      first = tasks.begin[i];
-    }
+    for (int i = 4; i < kMaxTasks; ++i)
+      if (bx >= tasks.begin[i]) {
+        ti = i;
+        first = tasks.begin[i];
+      }
+  } else if (bx >= begin2) {
+    ti = 2;
+    first = begin2;
+  } else if (bx >= begin1) {
+    ti = 1;
+    first = begin1;
+  }
   const GemvTask& task = tasks.t[ti];
   // Every field of the task in scalar registers at once: used one by one,
   // the compiler spreads their loads over several dependent round trips.
@@ -614,7 +628,8 @@ hipError_t launch_k(dim3 grid, size_t lds, hipStream_t s, const GemvTasks& ts) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_gemv_m1<L, P, kU, NT, MX>), grid, dim3(kBlock), lds, s, ts);
+  hipLaunchKernelGGL((k_gemv_m1<L, P, kU, NT, MX>), grid, dim3(kBlock), lds, s, ts.begin[1], ts.begin[2],
+                     ts.begin[3], ts);
   return hipGetLastError();
 }
 
