@@ -24,8 +24,8 @@ ARCH = "gfx950"
 SOURCES = {
     "abi.hip": [],
     "pack.hip": ["-ffp-contract=off"],
-    # the kernel's three leading task boundaries land in scalar registers at launch
-    "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=3"],
+    # the GEMV's 14 leading scalar arguments land in scalar registers at launch
+    "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"],
     "mfma.hip": [],
     "embed.hip": [],
     "kv.hip": ["-ffp-contract=off"],

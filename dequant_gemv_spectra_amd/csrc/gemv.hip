@@ -75,17 +75,17 @@ struct GemvTask {
   int32_t rows_per_block;  // contiguous rows per block (short launches), else 0
 };
 
-// Kernel arguments.  The first blocks of tasks 1 .. 3 also come as three
+// Kernel arguments.  Task 0 (its container base, x, y, N, K, n_out and row
+// split), the rows of x and the first blocks of tasks 1 .. 3 come as 14
 // leading scalar arguments, which the build preloads into scalar registers
-// (kernarg preloading, -amdgpu-kernarg-preload-count=3): a block of the first
-// four tasks finds its task with no memory access and then reads that task's
-// fields in one batch of scalar loads, a single round trip to the argument
-// memory before its first vector load.  Tasks 4 .. 7 read `begin` first.
+// (kernarg preloading, -amdgpu-kernarg-preload-count=14).  A block of task 0
+// (every block of a one-container launch) computes its section addresses from
+// the base and the shape and touches no argument memory; a block of tasks
+// 1 .. 3 reads its task's fields below in one batch of scalar loads, a single
+// round trip before its first vector load; tasks 4 .. 7 read `begin` first.
 struct GemvTasks {
   int32_t begin[kMaxTasks];  // first block of each task; INT32_MAX past the last task
   int32_t count;
-  uint32_t nib_lo, nib_hi, mag_lo, mag_hi;  // see Nib
-  int32_t m_rows;                           // rows of x (and y) of the launch, <= MX
   GemvTask t[kMaxTasks];
 };
 
@@ -127,11 +127,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
 }
 
-// Nibble masks and fp16 magics of a code word.  The masks arrive as kernel
-// arguments (scalar registers) and the magics are moved into vector registers
-// once, so that each (w & mask) | magic compiles to one v_and_or_b32: a gfx9
-// VOP3 encoding takes no literal, and with immediates the compiler emits a
-// separate AND and OR.
+// Nibble masks and fp16 magics of a code word.  The masks sit in scalar
+// registers and the magics in vector registers, each written once by an
+// opaque move, so that each (w & mask) | magic compiles to one v_and_or_b32:
+// a gfx9 VOP3 encoding takes no literal, and with immediates the compiler
+// emits a separate AND and OR.
 struct Nib {
   uint32_t lo, hi;    // 0x000F000F and 0x00F000F0
   uint32_t mlo, mhi;  // 0x64006400 (1024) and 0x54005400 (64)
@@ -425,41 +425,76 @@ __device__ __forceinline__ void compute_frag(const Frag<P, U, OS>& f, const Devi
 //
 // MX rows of x (a batch tile, M <= MX) share every dequantized record.
 template <int L, int P, int U, int NT, int MX>
-__global__ __launch_bounds__(kBlock) void k_gemv_m1(const int32_t begin1, const int32_t begin2,
+__global__ __launch_bounds__(kBlock) void k_gemv_m1(const unsigned char* base0, const uint16_t* x0, uint16_t* y0,
+                                                    const int32_t N0, const int32_t K0, const int32_t n_out0,
+                                                    const int32_t spread0, const int32_t m_rows,
+                                                    const int32_t begin1, const int32_t begin2,
                                                     const int32_t begin3, const GemvTasks tasks) {
   constexpr int OS = (L == 16) ? 4 : 2;  // heavy-tailed slots per lane held in registers
   constexpr int T = kBlock / L;          // teams per block
   constexpr int kTileRows = T * U;
   extern __shared__ __align__(16) unsigned char smem[];
-  int ti = 0, first = 0;  // the block's task and that task's first block
+  DeviceView v;
+  const uint16_t* xp;
+  uint16_t* yp;
+  int32_t spread;  // NT >= 1: rows per block; NT == 0: blocks of the task
+  int first = 0;   // the task's first block
   const int32_t bx = (int32_t)blockIdx.x;
-  if (bx >= begin3) {
-    ti = 3;
-    first = begin3;
-#pragma unroll
-    for (int i = 4; i < kMaxTasks; ++i)
-      if (bx >= tasks.begin[i]) {
-        ti = i;
-        first = tasks.begin[i];
-      }
-  } else if (bx >= begin2) {
-    ti = 2;
-    first = begin2;
-  } else if (bx >= begin1) {
-    ti = 1;
+  if (bx < begin1) {
+    // task 0 from the preloaded arguments alone: section addresses from the
+    // container base and the shape, no memory access
+    const Layout lay = make_layout(K0, N0, n_out0);
+    v.codes = reinterpret_cast<const uint4*>(base0 + lay.codes);
+    v.scales = reinterpret_cast<const uint16_t*>(base0 + lay.scales);
+    v.zeros = base0 + lay.zeros;
+    v.outliers = reinterpret_cast<const uint16_t*>(base0 + lay.outliers);
+    v.perm = reinterpret_cast<const int32_t*>(base0 + lay.perm);
+    v.mask = reinterpret_cast<const uint32_t*>(base0 + lay.mask);
+    v.N = N0;
+    v.K = K0;
+    v.n_out = n_out0;
+    v.K_b = K0 - n_out0;
+    v.G = (v.K_b + kGroup - 1) / kGroup;
+    v.cu_count = 0;
+    v.lds_per_block = 0;
+    xp = x0;
+    yp = y0;
+    spread = spread0;
+  } else {
+    int ti = 1;
     first = begin1;
+    if (bx >= begin3) {
+      ti = 3;
+      first = begin3;
+#pragma unroll
+      for (int i = 4; i < kMaxTasks; ++i)
+        if (bx >= tasks.begin[i]) {
+          ti = i;
+          first = tasks.begin[i];
+        }
+    } else if (bx >= begin2) {
+      ti = 2;
+      first = begin2;
+    }
+    const GemvTask& task = tasks.t[ti];
+    // Every field of the task in scalar registers at once: used one by one,
+    // the compiler spreads their loads over several dependent round trips.
+    asm volatile("" ::"s"(task.v.codes), "s"(task.v.scales), "s"(task.v.zeros), "s"(task.v.outliers),
+                 "s"(task.v.perm), "s"(task.x), "s"(task.y), "s"(task.v.N), "s"(task.v.K), "s"(task.v.K_b),
+                 "s"(task.v.G), "s"(task.v.n_out), "s"(task.nblocks), "s"(task.rows_per_block));
+    v = task.v;
+    xp = task.x;
+    yp = task.y;
+    spread = NT ? task.rows_per_block : task.nblocks;
   }
-  const GemvTask& task = tasks.t[ti];
-  // Every field of the task in scalar registers at once: used one by one,
-  // the compiler spreads their loads over several dependent round trips.
-  asm volatile("" ::"s"(task.v.codes), "s"(task.v.scales), "s"(task.v.zeros), "s"(task.v.outliers),
-               "s"(task.v.perm), "s"(task.x), "s"(task.y), "s"(task.v.N), "s"(task.v.K), "s"(task.v.K_b),
-               "s"(task.v.G), "s"(task.v.n_out), "s"(task.nblocks), "s"(task.rows_per_block));
-  uint32_t mlo, mhi;  // opaque copies: the compiler cannot fold them back into literals
-  asm volatile("v_mov_b32 %0, %1" : "=v"(mlo) : "s"(tasks.mag_lo));
-  asm volatile("v_mov_b32 %0, %1" : "=v"(mhi) : "s"(tasks.mag_hi));
-  const Nib nb{tasks.nib_lo, tasks.nib_hi, mlo, mhi};
-  const DeviceView& v = task.v;
+  // Nibble masks in scalar registers and fp16 magics in vector registers,
+  // written so the compiler cannot fold them back into literals (see Nib).
+  uint32_t nlo, nhi, mlo, mhi;
+  asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(nlo));
+  asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(nhi));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(mlo));
+  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(mhi));
+  const Nib nb{nlo, nhi, mlo, mhi};
   const int G = v.G, n_out = v.n_out;
   const int xstride = ((kXSlot * G + n_out) + 7) & ~7;  // halves per x row; 16-byte multiple
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
@@ -469,15 +504,15 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const int32_t begin1, const 
   const int team = tid / L;
   const int64_t lb = (int64_t)((int32_t)blockIdx.x - first);
   // NT >= 1: rows [row, end) in tiles of kTileRows; NT == 0: tiles `stride` apart
-  const int64_t stride = NT ? (int64_t)kTileRows : (int64_t)task.nblocks * kTileRows;
-  int64_t row = NT ? lb * task.rows_per_block : lb * kTileRows;
-  const int64_t end = NT ? (row + task.rows_per_block < v.N ? row + task.rows_per_block : v.N) : v.N;
+  const int64_t stride = NT ? (int64_t)kTileRows : (int64_t)spread * kTileRows;
+  int64_t row = NT ? lb * spread : lb * kTileRows;
+  const int64_t end = NT ? (row + spread < v.N ? row + spread : v.N) : v.N;
 
   // The first tile's weights are requested right behind the x and perm
   // loads, so their HBM latency overlaps the gather and the barriers.
   Frag<P, U, OS> fa, fb;
   half2_t xreg[P][16];  // used by the long loop with one row of x
-  stage_x<MX>(v, task.x, tasks.m_rows, xs, xstride, xraw, tid, [&] {
+  stage_x<MX>(v, xp, m_rows, xs, xstride, xraw, tid, [&] {
     __builtin_amdgcn_sched_barrier(0);
     load_frag<L, P, U, OS>(fa, v, row, end, lt, team);
     __builtin_amdgcn_sched_barrier(0);
@@ -516,8 +551,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const int32_t begin1, const 
       if (t + 1 < NT) load_frag<L, P, U, OS>(nxt, v, row + (t + 1) * stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
       if (row + t * stride < end)
-        compute_frag<L, P, U, OS, MX, XR>(cur, v, row + t * stride, end, lt, team, xs, xstride, xor_, tasks.m_rows,
-                                          task.y, nb, xreg);
+        compute_frag<L, P, U, OS, MX, XR>(cur, v, row + t * stride, end, lt, team, xs, xstride, xor_, m_rows, yp,
+                                          nb, xreg);
     }
   } else {
     // One row of x: this lane's groups of x stay in registers across the
@@ -533,12 +568,12 @@ __global__ __launch_bounds__(kBlock) void k_gemv_m1(const int32_t begin1, const 
     for (; row < v.N; row += 2 * stride) {
       load_frag<L, P, U, OS>(fb, v, row + stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
-      compute_frag<L, P, U, OS, MX, XR>(fa, v, row, end, lt, team, xs, xstride, xor_, tasks.m_rows, task.y, nb,
+      compute_frag<L, P, U, OS, MX, XR>(fa, v, row, end, lt, team, xs, xstride, xor_, m_rows, yp, nb,
                                         xreg);
       load_frag<L, P, U, OS>(fa, v, row + 2 * stride, end, lt, team);
       __builtin_amdgcn_sched_barrier(0);
       if (row + stride < v.N)
-        compute_frag<L, P, U, OS, MX, XR>(fb, v, row + stride, end, lt, team, xs, xstride, xor_, tasks.m_rows, task.y,
+        compute_frag<L, P, U, OS, MX, XR>(fb, v, row + stride, end, lt, team, xs, xstride, xor_, m_rows, yp,
                                           nb, xreg);
     }
   }
@@ -622,19 +657,23 @@ int64_t plan_blocks(GemvTasks& ts, int64_t per_cu) {
 }
 
 template <int L, int P, int NT, int MX>
-hipError_t launch_k(dim3 grid, size_t lds, hipStream_t s, const GemvTasks& ts) {
+hipError_t launch_k(dim3 grid, size_t lds, hipStream_t s, const GemvTasks& ts, int32_t m_rows) {
   const void* fn = reinterpret_cast<const void*>(&k_gemv_m1<L, P, kU, NT, MX>);
   if (lds > 64 * 1024) {  // dynamic LDS past 64 KiB must be allowed per kernel
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_gemv_m1<L, P, kU, NT, MX>), grid, dim3(kBlock), lds, s, ts.begin[1], ts.begin[2],
-                     ts.begin[3], ts);
+  const DeviceView& v0 = ts.t[0].v;
+  const Layout lay = make_layout(v0.K, v0.N, v0.n_out);
+  const unsigned char* base0 = reinterpret_cast<const unsigned char*>(v0.codes) - lay.codes;
+  const int32_t spread0 = NT ? ts.t[0].rows_per_block : ts.t[0].nblocks;
+  hipLaunchKernelGGL((k_gemv_m1<L, P, kU, NT, MX>), grid, dim3(kBlock), lds, s, base0, ts.t[0].x, ts.t[0].y,
+                     (int32_t)v0.N, v0.K, v0.n_out, spread0, m_rows, ts.begin[1], ts.begin[2], ts.begin[3], ts);
   return hipGetLastError();
 }
 
 template <int L, int P, int MX>
-hipError_t launch_lp(GemvTasks& ts, size_t lds, hipStream_t s) {
+hipError_t launch_lp(GemvTasks& ts, size_t lds, hipStream_t s, int32_t m_rows) {
   constexpr int64_t kTileRows = (int64_t)(kBlock / L) * kU;
   int64_t blocks = plan_blocks(ts, SPECTRA_GEMV_BLOCKS_PER_CU);
   int64_t most = 0, all_tiles = 0;  // most tiles any block walks when blocks take whole tiles in turn
@@ -657,7 +696,7 @@ hipError_t launch_lp(GemvTasks& ts, size_t lds, hipStream_t s) {
         blocks = plan_blocks(ts, 2);
     }
     for (int i = 0; i < ts.count; ++i) ts.t[i].rows_per_block = 0;
-    return launch_k<L, P, 0, MX>(dim3((unsigned)blocks), lds, s, ts);
+    return launch_k<L, P, 0, MX>(dim3((unsigned)blocks), lds, s, ts, m_rows);
   }
   const dim3 grid((unsigned)blocks);
   // Short launch: equal row ranges per block, at most nt tiles each.
@@ -669,11 +708,11 @@ hipError_t launch_lp(GemvTasks& ts, size_t lds, hipStream_t s) {
     nt = t > nt ? t : nt;
   }
   switch (nt) {
-    case 1: return launch_k<L, P, 1, 1>(grid, lds, s, ts);
-    case 2: return launch_k<L, P, 2, 1>(grid, lds, s, ts);
-    case 3: return launch_k<L, P, 3, 1>(grid, lds, s, ts);
-    case 4: return launch_k<L, P, 4, 1>(grid, lds, s, ts);
-    default: return launch_k<L, P, 5, 1>(grid, lds, s, ts);
+    case 1: return launch_k<L, P, 1, 1>(grid, lds, s, ts, m_rows);
+    case 2: return launch_k<L, P, 2, 1>(grid, lds, s, ts, m_rows);
+    case 3: return launch_k<L, P, 3, 1>(grid, lds, s, ts, m_rows);
+    case 4: return launch_k<L, P, 4, 1>(grid, lds, s, ts, m_rows);
+    default: return launch_k<L, P, 5, 1>(grid, lds, s, ts, m_rows);
   }
 }
 
@@ -681,45 +720,40 @@ hipError_t launch_lp(GemvTasks& ts, size_t lds, hipStream_t s) {
 constexpr int max_slots(int mx) { return mx >= 4 ? 4 : 8; }
 
 template <int L, int MX>
-hipError_t launch_l(int P, GemvTasks& ts, size_t lds, hipStream_t s) {
+hipError_t launch_l(int P, GemvTasks& ts, size_t lds, hipStream_t s, int32_t m_rows) {
   if constexpr (max_slots(MX) < 8) {
     switch (P) {
-      case 1: return launch_lp<L, 1, MX>(ts, lds, s);
-      case 2: return launch_lp<L, 2, MX>(ts, lds, s);
-      case 3: return launch_lp<L, 3, MX>(ts, lds, s);
-      case 4: return launch_lp<L, 4, MX>(ts, lds, s);
+      case 1: return launch_lp<L, 1, MX>(ts, lds, s, m_rows);
+      case 2: return launch_lp<L, 2, MX>(ts, lds, s, m_rows);
+      case 3: return launch_lp<L, 3, MX>(ts, lds, s, m_rows);
+      case 4: return launch_lp<L, 4, MX>(ts, lds, s, m_rows);
       default: return hipErrorNotSupported;
     }
   } else {
     switch (P) {
-      case 1: return launch_lp<L, 1, MX>(ts, lds, s);
-      case 2: return launch_lp<L, 2, MX>(ts, lds, s);
-      case 3: return launch_lp<L, 3, MX>(ts, lds, s);
-      case 4: return launch_lp<L, 4, MX>(ts, lds, s);
-      case 5: return launch_lp<L, 5, MX>(ts, lds, s);
-      case 6: return launch_lp<L, 6, MX>(ts, lds, s);
-      case 7: return launch_lp<L, 7, MX>(ts, lds, s);
-      case 8: return launch_lp<L, 8, MX>(ts, lds, s);
+      case 1: return launch_lp<L, 1, MX>(ts, lds, s, m_rows);
+      case 2: return launch_lp<L, 2, MX>(ts, lds, s, m_rows);
+      case 3: return launch_lp<L, 3, MX>(ts, lds, s, m_rows);
+      case 4: return launch_lp<L, 4, MX>(ts, lds, s, m_rows);
+      case 5: return launch_lp<L, 5, MX>(ts, lds, s, m_rows);
+      case 6: return launch_lp<L, 6, MX>(ts, lds, s, m_rows);
+      case 7: return launch_lp<L, 7, MX>(ts, lds, s, m_rows);
+      case 8: return launch_lp<L, 8, MX>(ts, lds, s, m_rows);
       default: return hipErrorNotSupported;
     }
   }
 }
 
 template <int MX>
-hipError_t launch_mx(int L, int P, GemvTasks& ts, size_t lds, hipStream_t s) {
+hipError_t launch_mx(int L, int P, GemvTasks& ts, size_t lds, hipStream_t s, int32_t m_rows) {
   switch (L) {
-    case 16: return launch_l<16, MX>(P, ts, lds, s);
-    case 32: return launch_l<32, MX>(P, ts, lds, s);
-    default: return launch_l<64, MX>(P, ts, lds, s);
+    case 16: return launch_l<16, MX>(P, ts, lds, s, m_rows);
+    case 32: return launch_l<32, MX>(P, ts, lds, s, m_rows);
+    default: return launch_l<64, MX>(P, ts, lds, s, m_rows);
   }
 }
 
 hipError_t launch_tasks(GemvTasks& ts, int64_t M, hipStream_t s) {
-  ts.nib_lo = 0x000F000Fu;
-  ts.nib_hi = 0x00F000F0u;
-  ts.mag_lo = 0x64006400u;
-  ts.mag_hi = 0x54005400u;
-  ts.m_rows = (int32_t)M;
   const int mx = batch_tile(M);
   int gmax = 0;
   size_t lds = 0;
@@ -731,9 +765,9 @@ hipError_t launch_tasks(GemvTasks& ts, int64_t M, hipStream_t s) {
   const Variant vr = pick_variant(gmax);
   if (vr.P == 0 || lds > lds_limit(ts.t[0].v)) return hipErrorNotSupported;
   switch (mx) {
-    case 1: return launch_mx<1>(vr.L, vr.P, ts, lds, s);
-    case 2: return launch_mx<2>(vr.L, vr.P, ts, lds, s);
-    default: return launch_mx<4>(vr.L, vr.P, ts, lds, s);
+    case 1: return launch_mx<1>(vr.L, vr.P, ts, lds, s, (int32_t)M);
+    case 2: return launch_mx<2>(vr.L, vr.P, ts, lds, s, (int32_t)M);
+    default: return launch_mx<4>(vr.L, vr.P, ts, lds, s, (int32_t)M);
   }
 }
 
@@ -741,6 +775,7 @@ hipError_t launch_tasks(GemvTasks& ts, int64_t M, hipStream_t s) {
 
 bool gemv_supports(const DeviceView& v, int64_t M) {
   if (M < 1 || M > 4) return false;
+  if (v.N > INT32_MAX) return false;  // rows travel as a 32-bit kernel argument
   if (M > 1 && v.K % 8 != 0) return false;  // each row of x must start 16-byte aligned
   // a block stages at most kXChunks * 8 * kBlock channels and kQuads * 4 * kBlock bulk positions
   if (v.K > kXChunks * 8 * kBlock || (int64_t)kGroup * v.G > (int64_t)kQuads * 4 * kBlock) return false;

@@ -22,9 +22,9 @@ struct Layout {
   uint64_t mask, perm, codes, scales, zeros, outliers, total;
 };
 
-inline uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+__host__ __device__ inline uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-inline Layout make_layout(int64_t K, int64_t N, int64_t n_out) {
+__host__ __device__ inline Layout make_layout(int64_t K, int64_t N, int64_t n_out) {
   const int64_t K_b = K - n_out;
   const int64_t G = (K_b + kGroup - 1) / kGroup;
   const uint64_t NG = (uint64_t)N * (uint64_t)G;
