@@ -28,7 +28,8 @@ SOURCES = {
     "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"],
     "mfma.hip": [],
     "embed.hip": [],
-    "kv.hip": ["-ffp-contract=off"],
+    # k_kv_combine's scalar arguments preloaded into scalar registers as well
+    "kv.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-kernarg-preload-count=14"],
 }
 
 COMMON = [
