@@ -173,7 +173,9 @@ int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t 
                     void* stream, int kernel);
 
 /* Which kernel spectra_gemm_ex would run for M rows of x and the selector
- * `kernel` (a spectra_kernel), without any device work.  Returns
+ * `kernel` (a spectra_kernel), without any device work: the product is the
+ * fused dequantize-and-multiply of spectra_gemm (SPECTRA page, abstract and
+ * highlight 4); this only reports how it would be launched.  Returns
  * SPECTRA_PLAN_GEMV, SPECTRA_PLAN_MFMA_TILED or SPECTRA_PLAN_MFMA; or, as
  * spectra_gemm_ex would, SPECTRA_E_INVAL (invalid container, M out of range,
  * unknown selector) or SPECTRA_E_UNSUPPORTED (a forced kernel that cannot run
