@@ -61,7 +61,6 @@ namespace {
 #define SPECTRA_GEMV_BLOCK 512
 #endif
 constexpr int kBlock = SPECTRA_GEMV_BLOCK;
-constexpr int kWaves = kBlock / 64;
 constexpr int kMaxTasks = 8;
 constexpr int kXSlot = 40;  // halves per group slot in LDS (32 used, 80 bytes)
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
