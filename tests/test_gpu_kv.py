@@ -86,6 +86,16 @@ def test_attend_within_bound(H, rep, D, L, seed):
     _attend_case(H, rep, D, L, seed)
 
 
+# One split exactly and one token past it (128 tokens per split), then more
+# splits than the combine requests in its first round of loads (32 * 256 / D:
+# 64 at D = 128, 32 at D = 256, 128 at D = 64), which walks the remaining
+# splits in a second loop.
+@pytest.mark.parametrize("H,rep,D,L,seed", [(1, 2, 128, 128, 20), (1, 2, 128, 129, 21), (1, 4, 128, 8325, 22),
+                                            (2, 2, 256, 4500, 23), (1, 2, 64, 16600, 24)])
+def test_attend_split_boundaries(H, rep, D, L, seed):
+    _attend_case(H, rep, D, L, seed)
+
+
 def test_attend_peaked_scores():
     # large keys make the softmax nearly one-hot: the max subtraction matters
     _attend_case(2, 2, 128, 300, 15, k_scale=8.0)
