@@ -168,7 +168,10 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
   __shared__ half2_t qs[REP][D / 2];
   __shared__ float sc[REP][TS];
   __shared__ float mst[REP], lst[REP];
-  __shared__ float pacc[WAVES][D];
+  // all query heads' wave partials at once (one barrier) where they fit in
+  // 32 KiB, else one query head at a time
+  constexpr bool ALL = REP * D <= 2048;
+  __shared__ float pacc[WAVES][ALL ? REP : 1][D];
   const int split = blockIdx.x, h = blockIdx.y;
   const int H = c.H, Hq = H * rep;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -294,28 +297,53 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
       }
     }
   }
+  if constexpr (ALL) {
 #pragma unroll
-  for (int rr = 0; rr < REP; ++rr) {
+    for (int rr = 0; rr < REP; ++rr)
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int pi = lane + 64 * i;
-      if (pi < NP) {
-        pacc[wave][2 * pi] = a[rr][i][0];
-        pacc[wave][2 * pi + 1] = a[rr][i][1];
+      for (int i = 0; i < PL; ++i) {
+        const int pi = lane + 64 * i;
+        if (pi < NP) {
+          pacc[wave][rr][2 * pi] = a[rr][i][0];
+          pacc[wave][rr][2 * pi + 1] = a[rr][i][1];
+        }
       }
-    }
     __syncthreads();
-    const int64_t base = (int64_t)split * Hq + h * rep + rr;
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    for (int j = threadIdx.x; j < REP * D; j += blockDim.x) {
+      const int rr = j / D, d = j % D;
       float sum = 0.f;
-      for (int w2 = 0; w2 < WAVES; ++w2) sum += pacc[w2][d];
-      part[base * D + d] = sum;
+      for (int w2 = 0; w2 < WAVES; ++w2) sum += pacc[w2][rr][d];
+      part[((int64_t)split * Hq + h * rep + rr) * D + d] = sum;
     }
-    if (threadIdx.x == 0) {
-      stats[2 * base] = mst[rr];
-      stats[2 * base + 1] = lst[rr];
+    if (threadIdx.x < REP) {
+      const int64_t base = (int64_t)split * Hq + h * rep + threadIdx.x;
+      stats[2 * base] = mst[threadIdx.x];
+      stats[2 * base + 1] = lst[threadIdx.x];
     }
-    __syncthreads();
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < REP; ++rr) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int pi = lane + 64 * i;
+        if (pi < NP) {
+          pacc[wave][0][2 * pi] = a[rr][i][0];
+          pacc[wave][0][2 * pi + 1] = a[rr][i][1];
+        }
+      }
+      __syncthreads();
+      const int64_t base = (int64_t)split * Hq + h * rep + rr;
+      for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        float sum = 0.f;
+        for (int w2 = 0; w2 < WAVES; ++w2) sum += pacc[w2][0][d];
+        part[base * D + d] = sum;
+      }
+      if (threadIdx.x == 0) {
+        stats[2 * base] = mst[rr];
+        stats[2 * base + 1] = lst[rr];
+      }
+      __syncthreads();
+    }
   }
 }
 
