@@ -143,9 +143,10 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 //      first, 16 bytes of records per thread and load (as many small
 //      per-lane loads cost 3 % more); they are stored to LDS once the scores
 //      are done;
-//   2. threads 0 .. 127 take one token each: dequantize its key (exact fp16
-//      (q - z) pairs), dot it with the rep queries in fp32, times s16 per
-//      group, over sqrt(D) -> scores in LDS;
+//   2. two adjacent threads per token, G / 2 groups each: dequantize the
+//      key's groups (exact fp16 (q - z) pairs), dot them with the rep queries
+//      in fp32, times s16 per group; the pair adds its halves with one lane
+//      swap, over sqrt(D) -> scores in LDS;
 //   3. per query head the split's max m and l = sum exp(s - m); the scores
 //      become p = exp(s - m);
 //   4. sum_t p_t v_t per query head in registers (lane-per-channel-pair:
@@ -199,29 +200,31 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
   }
   __syncthreads();  // qs ready
 
-  // 2. scores: every key load of the token first, then the arithmetic
-  if (threadIdx.x < TS) {
-    const int tl = threadIdx.x;
+  // 2. scores: two threads per token (adjacent lanes), G / 2 groups each
+  static_assert(2 * TS == kPvThreads, "two threads per token");
+  {
+    constexpr int GH = G / 2;
+    const int tl = threadIdx.x >> 1, hf = threadIdx.x & 1;
     const int64_t t = t0 + tl;
-    const int64_t flat0 = ((t < L ? t : t0) * H + h) * G;
-    uint4 krec[G];
-    uint16_t ksc[G];
-    uint8_t kzb[G / 2];
+    const int64_t flat0 = ((t < L ? t : t0) * H + h) * G + hf * GH;
+    uint4 krec[GH];
+    uint16_t ksc[GH];
+    uint8_t kzb[GH];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < GH; ++g) {
       krec[g] = c.k.codes[flat0 + g];
       ksc[g] = c.k.scales[flat0 + g];
+      kzb[g] = c.k.zeros[(flat0 + g) >> 1];
     }
-#pragma unroll
-    for (int g = 0; g < G; g += 2) kzb[g / 2] = c.k.zeros[(flat0 + g) >> 1];
     float acc[REP];
 #pragma unroll
     for (int rr = 0; rr < REP; ++rr) acc[rr] = 0.f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float s16 = h2f(ksc[g]);
-      const uint32_t z = ((uint32_t)kzb[g / 2] >> (4 * (g & 1))) & 0xFu;
-      const uint32_t w[4] = {krec[g].x, krec[g].y, krec[g].z, krec[g].w};
+    for (int gg = 0; gg < GH; ++gg) {
+      const int g = hf * GH + gg;
+      const float s16 = h2f(ksc[gg]);
+      const uint32_t z = ((uint32_t)kzb[gg] >> (4 * (g & 1))) & 0xFu;
+      const uint32_t w[4] = {krec[gg].x, krec[gg].y, krec[gg].z, krec[gg].w};
       half2_t wq[16];
 #pragma unroll
       for (int d = 0; d < 4; ++d)
@@ -238,9 +241,13 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
         acc[rr] = __builtin_fmaf(s16, a0 + a1, acc[rr]);
       }
     }
-    const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
 #pragma unroll
-    for (int rr = 0; rr < REP; ++rr) sc[rr][tl] = t < L ? acc[rr] * inv_sqrt_d : -INFINITY;
+    for (int rr = 0; rr < REP; ++rr) acc[rr] += __shfl_xor(acc[rr], 1);
+    const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
+    if (hf == 0) {
+#pragma unroll
+      for (int rr = 0; rr < REP; ++rr) sc[rr][tl] = t < L ? acc[rr] * inv_sqrt_d : -INFINITY;
+    }
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
