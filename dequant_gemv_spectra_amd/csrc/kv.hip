@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
   for (int rr = 0; rr < REP; ++rr)
 #pragma unroll
     for (int i = 0; i < PL; ++i) a[rr][i][0] = a[rr][i][1] = 0.f;
-#pragma unroll 4
+#pragma unroll 2
   for (int u = 0; u < UN; ++u) {
     const int tl = wave + WAVES * u;
 #pragma unroll
