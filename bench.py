@@ -6,9 +6,15 @@
 Default workload (cfg3): the M = 1 decode step of a 4B-class decoder -- 36
 layers x 7 linears (q/k/v/o/gate/up/down, hidden 2560, MLP 9728), every layer
 distinct, so one step streams about 2.2 GB of packed weights from HBM.
-Same-input projections run as one grouped launch (q/k/v and gate/up): 4
-launches per layer, 144 per step, replayed as one captured HIP graph.
-Containers and inputs are resident in HBM before timing starts.
+Default mode `graph`: the products as 144 launches (q/k/v and gate/up
+grouped) replayed as one captured HIP graph, each launch on its own
+synthetic input.  Mode `step`: the whole step is one launch of the
+persistent decode-step kernel (spectra_step_run): 144 dependent phases
+(q/k/v, o, gate/up, down per layer), each phase reading the previous one's
+output (o reads q, gate/up read o, down reads gate, the next q/k/v read
+down, each scaled by a power of two; the attention, norms and activation
+between them are outside the path).  Containers and inputs are resident in
+HBM before timing starts.
 
 value = algorithmic bytes per step / step time.  A linear's algorithmic bytes
 are its container payload (codes + scales + zero nibbles + fp16 heavy-tailed
@@ -57,6 +63,8 @@ def parse():
     ap.add_argument("--context", type=int, default=8192, help="kv: cached tokens attended per step")
     ap.add_argument("--M", type=int, default=1)
     ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "mfma"])
+    ap.add_argument("--mode", default="graph", choices=["step", "graph"],
+                    help="cfg2/cfg3 at M = 1: a graph of 144 launches, or one persistent launch per step")
     ap.add_argument("--layers", type=int, default=None, help="cfg3: fewer layers (quick runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
@@ -83,9 +91,14 @@ class Linear:
     """One packed linear with resident x and y."""
 
     def __init__(self, sp, torch, lin, cfg, M, W=None, g=None, copy=0):
+        import numpy as np
         from dequant_gemv_spectra_amd import synth
         W = synth.weights(lin, cfg) if W is None else W
         g = synth.gamma(lin, cfg) if g is None else g
+        # rms gain of the product for unit-rms input (row norms of W): sets the
+        # decode-step chain's power-of-two input scales
+        w = W.astype(np.float32).ravel()
+        self.gain = float(np.sqrt(np.dot(w, w) / lin.N))
         self.c = sp.spectra_pack(W, g)
         self.info = self.c.info()
         self.lin = lin
@@ -132,6 +145,7 @@ def build_units(args, sp, torch):
     wl = synth.workload(cfg, layers=args.layers if cfg == 3 else None)
     M, kern = args.M, args.kernel
     units = []
+    args.layers_packed = []
     if cfg in (2, 3):
         by_layer = {}
         for lin in wl.linears:
@@ -148,6 +162,7 @@ def build_units(args, sp, torch):
                     W, g = cache[lin.name]
                     packed.append(Linear(sp, torch, lin, cfg, M, W, g, copy=cp))
                 units.extend(layer_units(sp, packed, M, kern, f"L{layer if depth == 1 else cp}"))
+                args.layers_packed.append({p.lin.name.split(".")[-1]: p for p in packed})
                 if (layer if depth == 1 else cp) % 6 == 0:
                     log(f"layer {layer if depth == 1 else cp}: packed in {time.time() - t0:.1f}s")
             if depth == 1:
@@ -323,6 +338,59 @@ def run_kv(args, sp, torch):
     print(json.dumps(out), flush=True)
 
 
+def run_step(args, sp, torch, name, units):
+    """Mode `step`: the decoder stack as one persistent launch per step."""
+    from dequant_gemv_spectra_amd import decoder
+    layers, gains = [], []
+    for L in args.layers_packed:
+        layers.append({nm: (p.c, p.y.view(-1)) for nm, p in L.items()})
+        gains += [L["q"].gain, L["o"].gain, L["gate"].gain, L["down"].gain]
+    x0 = args.layers_packed[0]["q"].x.view(-1)
+    phases = decoder.layer_phases(layers, x0, decoder.chain_scales(gains))
+    plan = sp.StepPlan(phases)
+    # algorithmic bytes: every container's payload + metadata, each phase's
+    # input once, every output once
+    step_bytes = 0
+    for ph in phases:
+        K = ph["containers"][0].info()["K"]
+        step_bytes += 2 * K
+        for c in ph["containers"]:
+            inf = c.info()
+            step_bytes += inf["bytes_payload"] + inf["bytes_meta"] + 2 * inf["N"]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(args.warmup):
+            plan.run(stream=s)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    z = torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(args.steps):
+        plan.run(stream=s)
+    z.record(s)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(z) / args.steps
+    if plan.status(stream=s) != sp.SPECTRA_OK:
+        print(json.dumps({"error": "a wait inside the decode step gave up; the run is invalid"}))
+        sys.exit(3)
+    value = step_bytes / (ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "k_step (the whole step is one launch)", "avg_launch_us": round(ms * 1e3, 3),
+                "bytes_per_launch": int(step_bytes), "launches_timed": args.steps}
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        ent = tr.get("entries", {}).get(f"{args.workload}:M1:step")
+        if ent and ent.get("source_sha") == kernel_sources_sha(("step.hip", "gemv_common.h", "spectra_internal.h")):
+            roofline["traffic"] = int(ent["hbm_bytes_per_launch"])
+    except (OSError, ValueError):
+        pass
+    plan.close()
+    return ms, value, step_bytes, len(phases), roofline
+
+
 _CAPTURE_STREAM = None
 
 
@@ -385,6 +453,19 @@ def cpu_baseline(metas, min_s=10.0):
                       f"cores = BLAS threads of the product (the unpack is single-threaded numpy)"}
 
 
+def cpu_baseline_for(args, sp, cfg):
+    from dequant_gemv_spectra_amd import synth
+    wl = synth.workload(cfg, layers=1 if cfg == 3 else None)
+    metas = []
+    for lin in (wl.linears[:7] if cfg in (2, 3) else wl.linears[:1]):
+        c = sp.spectra_pack(synth.weights(lin, cfg), synth.gamma(lin, cfg))
+        info = c.info()
+        nbytes = info["bytes_payload"] + info["bytes_meta"] + 2 * args.M * (lin.K + lin.N)
+        metas.append((lin.name, sp.spectra_export(c), synth.activations(lin, cfg, args.M), nbytes))
+        c.close()
+    return cpu_baseline(metas)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -423,6 +504,19 @@ def main():
     log(f"setup {time.time() - t0:.1f}s, {len(units)} launches per pass")
 
     pass_bytes = sum(u[3] for u in units)
+    if layered and args.M == 1 and args.mode == "step" and not args.eager:
+        ms_per_step, value, bytes_per_step, nph, roofline = run_step(args, sp, torch, name, units)
+        cpu = None if args.no_cpu_baseline else cpu_baseline_for(args, sp, cfg)
+        out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+               "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+               "config": {"workload": name, "M": 1, "launches_per_step": 1, "phases_per_step": nph,
+                          "bytes_per_step": int(bytes_per_step),
+                          "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2), "mode": "step",
+                          "kernel": "k_step", "parallelism": "single GPU"},
+               "roofline": roofline, "cpu_baseline": cpu}
+        print(json.dumps(out), flush=True)
+        return
     if args.eager:  # counter runs: plain launches, no graphs, no timing claims
         for _ in range(max(1, args.steps)):
             for u in units:
@@ -483,18 +577,7 @@ def main():
     except (OSError, ValueError):
         pass
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        from dequant_gemv_spectra_amd import synth
-        wl = synth.workload(cfg, layers=1 if cfg == 3 else None)
-        metas = []
-        for lin in (wl.linears[:7] if cfg in (2, 3) else wl.linears[:1]):
-            c = sp.spectra_pack(synth.weights(lin, cfg), synth.gamma(lin, cfg))
-            info = c.info()
-            nbytes = info["bytes_payload"] + info["bytes_meta"] + 2 * args.M * (lin.K + lin.N)
-            metas.append((lin.name, sp.spectra_export(c), synth.activations(lin, cfg, args.M), nbytes))
-            c.close()
-        cpu = cpu_baseline(metas)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_for(args, sp, cfg)
 
     out = {
         "metric": METRIC,
@@ -512,7 +595,8 @@ def main():
         "config": {"workload": name, "M": args.M, "launches_per_step": launches,
                    "bytes_per_step": int(bytes_per_step),
                    "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
-                   "hip_graph": True, "kernel": args.kernel, "parallelism": "single GPU"},
+                   "hip_graph": True, "mode": "graph" if layered else "launches", "kernel": args.kernel,
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -27,6 +27,7 @@ SOURCES = {
     # the GEMV's 14 leading scalar arguments land in scalar registers at launch
     "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"],
     "mfma.hip": [],
+    "step.hip": [],
     "embed.hip": [],
     # k_kv_combine's scalar arguments preloaded into scalar registers as well
     "kv.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-kernarg-preload-count=14"],
@@ -63,7 +64,7 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max(1, jobs)) as ex:
         objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], verbose), SOURCES.items()))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

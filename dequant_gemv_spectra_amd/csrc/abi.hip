@@ -10,7 +10,7 @@
 #include <map>
 #include <mutex>
 #include <new>
-#include <unordered_set>
+#include <unordered_map>
 #include <utility>
 #include <vector>
 
@@ -21,6 +21,7 @@ namespace spectra {
 
 namespace {
 thread_local std::string g_last_error;
+thread_local int g_last_status = SPECTRA_OK;
 
 struct PropsCache {
   std::mutex mu;
@@ -33,10 +34,13 @@ PropsCache& props_cache() {
 }
 }  // namespace
 
-void set_error(const std::string& msg) { g_last_error = msg; }
+void set_error(const std::string& msg, int status) {
+  g_last_error = msg;
+  g_last_status = msg.empty() ? SPECTRA_OK : status;
+}
 
 int fail(int status, const std::string& msg) {
-  set_error(msg);
+  set_error(msg, status);
   return status;
 }
 
@@ -100,32 +104,41 @@ std::string hip_msg(const char* what, hipError_t e) {
   return std::string(what) + ": " + hipGetErrorString(e);
 }
 
-// Registry of live handles: a handle is checked by membership, so a freed or
-// foreign pointer is rejected without ever being dereferenced.
-struct Registry {
+// Handles.  The pointers the ABI hands out are identifiers, not addresses:
+// each is drawn once from a counter and never reissued, so a freed handle
+// stays invalid even when a later object lands at the same address, and a
+// handle is checked by lookup without ever being dereferenced.
+template <class T>
+struct HandleTable {
   std::mutex mu;
-  std::unordered_set<const spectra_container*> live;
+  std::unordered_map<uintptr_t, T*> objs;
+  uintptr_t next = 0x10000;
+  T* publish(T* o) {
+    std::lock_guard<std::mutex> lk(mu);
+    const uintptr_t h = next;
+    next += 16;
+    objs.emplace(h, o);
+    return reinterpret_cast<T*>(h);
+  }
+  T* get(const void* h) {
+    std::lock_guard<std::mutex> lk(mu);
+    const auto it = objs.find(reinterpret_cast<uintptr_t>(h));
+    return it == objs.end() ? nullptr : it->second;
+  }
+  T* retire(const void* h) {
+    std::lock_guard<std::mutex> lk(mu);
+    const auto it = objs.find(reinterpret_cast<uintptr_t>(h));
+    if (it == objs.end()) return nullptr;
+    T* o = it->second;
+    objs.erase(it);
+    return o;
+  }
 };
-Registry& registry() {
-  static Registry r;
-  return r;
+HandleTable<spectra_container>& containers() {
+  static HandleTable<spectra_container> t;
+  return t;
 }
-bool live(const spectra_container* c) {
-  if (c == nullptr) return false;
-  Registry& r = registry();
-  std::lock_guard<std::mutex> lk(r.mu);
-  return r.live.count(c) != 0;
-}
-void register_handle(const spectra_container* c) {
-  Registry& r = registry();
-  std::lock_guard<std::mutex> lk(r.mu);
-  r.live.insert(c);
-}
-bool unregister_handle(const spectra_container* c) {
-  Registry& r = registry();
-  std::lock_guard<std::mutex> lk(r.mu);
-  return r.live.erase(c) != 0;
-}
+spectra_container* cont(const spectra_container* h) { return containers().get(h); }
 
 // Frees device buffers on scope exit unless released.
 struct DevBuf {
@@ -155,36 +168,36 @@ spectra_container* pack_impl(const uint16_t* W_dev, const uint16_t* g_dev, int64
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) {
-    set_error(hip_msg("hipGetDevice", e));
+    set_error(hip_msg("hipGetDevice", e), SPECTRA_E_HIP);
     return nullptr;
   }
   const uint64_t mask_words = (uint64_t)((K + 31) / 32);
   DevBuf scratch, status;
   e = hipMalloc(&scratch.p, kurtosis_scratch_bytes(K, N));
   if (e != hipSuccess) {
-    set_error(hip_msg("hipMalloc (kurtosis scratch)", e));
+    set_error(hip_msg("hipMalloc (kurtosis scratch)", e), SPECTRA_E_NOMEM);
     return nullptr;
   }
   e = hipMalloc(&status.p, 4 * (1 + mask_words));
   if (e != hipSuccess) {
-    set_error(hip_msg("hipMalloc (status)", e));
+    set_error(hip_msg("hipMalloc (status)", e), SPECTRA_E_NOMEM);
     return nullptr;
   }
   uint32_t* st = static_cast<uint32_t*>(status.p);
   if ((e = hipMemsetAsync(st, 0, 4 * (1 + mask_words), s)) != hipSuccess ||
       (e = launch_kurtosis(W_dev, g_dev, K, N, scratch.p, st, s)) != hipSuccess) {
-    set_error(hip_msg("kurtosis launch", e));
+    set_error(hip_msg("kurtosis launch", e), SPECTRA_E_HIP);
     return nullptr;
   }
   std::vector<uint32_t> host_status(1 + mask_words);
   if ((e = hipMemcpyAsync(host_status.data(), st, 4 * (1 + mask_words), hipMemcpyDeviceToHost,
                           s)) != hipSuccess ||
       (e = hipStreamSynchronize(s)) != hipSuccess) {
-    set_error(hip_msg("kurtosis readback", e));
+    set_error(hip_msg("kurtosis readback", e), SPECTRA_E_HIP);
     return nullptr;
   }
   if (host_status[0] & 1u) {
-    set_error("W or gamma holds a non-finite value");
+    set_error("W or gamma holds a non-finite value", SPECTRA_E_NONFINITE);
     return nullptr;
   }
   int64_t n_out = 0;
@@ -192,7 +205,7 @@ spectra_container* pack_impl(const uint16_t* W_dev, const uint16_t* g_dev, int64
 
   spectra_container* c = new (std::nothrow) spectra_container();
   if (!c) {
-    set_error("host allocation of the container handle failed");
+    set_error("host allocation of the container handle failed", SPECTRA_E_NOMEM);
     return nullptr;
   }
   c->tag = kLiveTag;
@@ -207,7 +220,7 @@ spectra_container* pack_impl(const uint16_t* W_dev, const uint16_t* g_dev, int64
   e = hipMalloc(&img.p, c->lay.total);
   if (e != hipSuccess) {
     delete c;
-    set_error(hip_msg("hipMalloc (container)", e));
+    set_error(hip_msg("hipMalloc (container)", e), SPECTRA_E_NOMEM);
     return nullptr;
   }
   c->dev = static_cast<unsigned char*>(img.p);
@@ -234,12 +247,11 @@ spectra_container* pack_impl(const uint16_t* W_dev, const uint16_t* g_dev, int64
       (e = launch_quantize(W_dev, c, s)) != hipSuccess ||
       (e = hipStreamSynchronize(s)) != hipSuccess) {
     delete c;
-    set_error(hip_msg("packing", e));
+    set_error(hip_msg("packing", e), SPECTRA_E_HIP);
     return nullptr;
   }
   img.release();
-  register_handle(c);
-  return c;
+  return containers().publish(c);
 }
 
 // ---- container images on the host (files, import) ----
@@ -349,12 +361,12 @@ spectra_container* new_container(const ImageFields& f) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) {
-    set_error(hip_msg("hipGetDevice", e));
+    set_error(hip_msg("hipGetDevice", e), SPECTRA_E_HIP);
     return nullptr;
   }
   spectra_container* c = new (std::nothrow) spectra_container();
   if (!c) {
-    set_error("host allocation of the container handle failed");
+    set_error("host allocation of the container handle failed", SPECTRA_E_NOMEM);
     return nullptr;
   }
   c->tag = kLiveTag;
@@ -369,7 +381,7 @@ spectra_container* new_container(const ImageFields& f) {
   e = hipMalloc(&p, f.lay.total);
   if (e != hipSuccess) {
     delete c;
-    set_error(hip_msg("hipMalloc (container)", e));
+    set_error(hip_msg("hipMalloc (container)", e), SPECTRA_E_NOMEM);
     return nullptr;
   }
   c->dev = static_cast<unsigned char*>(p);
@@ -405,15 +417,6 @@ struct File {
 
 // ---- KV caches ----
 
-struct KvRegistry {
-  std::mutex mu;
-  std::unordered_set<const spectra_kv*> live;
-};
-KvRegistry& kv_registry() {
-  static KvRegistry r;
-  return r;
-}
-
 }  // namespace
 }  // namespace spectra
 
@@ -425,13 +428,19 @@ struct spectra_kv {
   uint64_t plane_bytes[3];  // per plane: records, scales, zeros (capacity-sized)
 };
 
+struct spectra_step {
+  spectra::StepPlan* plan;
+};
+
 namespace spectra {
 namespace {
-bool kv_live(const spectra_kv* kv) {
-  if (!kv) return false;
-  KvRegistry& r = kv_registry();
-  std::lock_guard<std::mutex> lk(r.mu);
-  return r.live.count(kv) != 0;
+HandleTable<spectra_kv>& kvs() {
+  static HandleTable<spectra_kv> t;
+  return t;
+}
+HandleTable<spectra_step>& steps() {
+  static HandleTable<spectra_step> t;
+  return t;
 }
 }  // namespace
 }  // namespace spectra
@@ -444,11 +453,13 @@ int spectra_version(void) { return 1; }
 
 const char* spectra_last_error(void) { return g_last_error.c_str(); }
 
+int spectra_last_status(void) { return g_last_status; }
+
 spectra_container* spectra_pack_device(const void* W, const void* gamma, int64_t K, int64_t N,
                                        void* stream) {
-  set_error("");
+  set_error("", SPECTRA_E_INVAL);
   if (!W || !gamma) {
-    set_error("null W or gamma");
+    set_error("null W or gamma", SPECTRA_E_INVAL);
     return nullptr;
   }
   if (check_shape(K, N) != SPECTRA_OK) return nullptr;
@@ -457,9 +468,9 @@ spectra_container* spectra_pack_device(const void* W, const void* gamma, int64_t
 }
 
 spectra_container* spectra_pack(const uint16_t* W, const uint16_t* gamma, int64_t K, int64_t N) {
-  set_error("");
+  set_error("", SPECTRA_E_INVAL);
   if (!W || !gamma) {
-    set_error("null W or gamma");
+    set_error("null W or gamma", SPECTRA_E_INVAL);
     return nullptr;
   }
   if (check_shape(K, N) != SPECTRA_OK) return nullptr;
@@ -467,20 +478,21 @@ spectra_container* spectra_pack(const uint16_t* W, const uint16_t* gamma, int64_
   hipError_t e;
   const size_t wbytes = 2ull * (uint64_t)N * (uint64_t)K;
   if ((e = hipMalloc(&wd.p, wbytes)) != hipSuccess || (e = hipMalloc(&gd.p, 2ull * K)) != hipSuccess) {
-    set_error(hip_msg("hipMalloc (staging W/gamma)", e));
+    set_error(hip_msg("hipMalloc (staging W/gamma)", e), SPECTRA_E_NOMEM);
     return nullptr;
   }
   if ((e = hipMemcpy(wd.p, W, wbytes, hipMemcpyHostToDevice)) != hipSuccess ||
       (e = hipMemcpy(gd.p, gamma, 2ull * K, hipMemcpyHostToDevice)) != hipSuccess) {
-    set_error(hip_msg("upload W/gamma", e));
+    set_error(hip_msg("upload W/gamma", e), SPECTRA_E_HIP);
     return nullptr;
   }
   return pack_impl(static_cast<const uint16_t*>(wd.p), static_cast<const uint16_t*>(gd.p), K, N,
                    nullptr);
 }
 
-void spectra_free(spectra_container* c) {
-  if (!unregister_handle(c)) return;
+void spectra_free(spectra_container* h) {
+  spectra_container* c = containers().retire(h);
+  if (!c) return;
   c->tag = kDeadTag;
   int cur = -1;
   (void)hipGetDevice(&cur);
@@ -491,8 +503,9 @@ void spectra_free(spectra_container* c) {
   delete c;
 }
 
-int spectra_info(const spectra_container* c, spectra_info_t* out) {
-  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+int spectra_info(const spectra_container* h, spectra_info_t* out) {
+  const spectra_container* c = cont(h);
+  if (!c) return fail(SPECTRA_E_INVAL, "invalid or freed container");
   if (!out) return fail(SPECTRA_E_INVAL, "null info pointer");
   const uint64_t NG = (uint64_t)c->N * (uint64_t)c->G;
   out->K = c->K;
@@ -510,8 +523,9 @@ int spectra_info(const spectra_container* c, spectra_info_t* out) {
   return SPECTRA_OK;
 }
 
-int spectra_export(const spectra_container* c, void* host_dst, uint64_t cap) {
-  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+int spectra_export(const spectra_container* h, void* host_dst, uint64_t cap) {
+  const spectra_container* c = cont(h);
+  if (!c) return fail(SPECTRA_E_INVAL, "invalid or freed container");
   if (!host_dst) return fail(SPECTRA_E_INVAL, "null destination");
   if (cap < c->lay.total) return fail(SPECTRA_E_INVAL, "destination smaller than total_bytes");
   hipError_t e = hipMemcpy(host_dst, c->dev, c->lay.total, hipMemcpyDeviceToHost);
@@ -536,7 +550,7 @@ int plan_of(const DeviceView& v, int64_t M, int kernel) {
 }
 
 int check_gemm_args(const spectra_container* c, int64_t M, int kernel) {
-  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+  if (!c) return fail(SPECTRA_E_INVAL, "invalid or freed container");
   if (M < 1 || M > SPECTRA_MAX_M) return fail(SPECTRA_E_INVAL, "M out of range [1, 2^20]");
   if (kernel < SPECTRA_KERNEL_AUTO || kernel > SPECTRA_KERNEL_MFMA)
     return fail(SPECTRA_E_INVAL, "unknown kernel selector");
@@ -545,15 +559,17 @@ int check_gemm_args(const spectra_container* c, int64_t M, int kernel) {
 
 }  // namespace
 
-int spectra_gemm_plan(const spectra_container* c, int64_t M, int kernel) {
+int spectra_gemm_plan(const spectra_container* h, int64_t M, int kernel) {
+  const spectra_container* c = cont(h);
   const int st = check_gemm_args(c, M, kernel);
   if (st != SPECTRA_OK) return st;
   return plan_of(c->view(), M, kernel);
 }
 
-int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t M, void* stream,
+int spectra_gemm_ex(const spectra_container* h, const void* x, void* y, int64_t M, void* stream,
                     int kernel) {
-  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+  const spectra_container* c = cont(h);
+  if (!c) return fail(SPECTRA_E_INVAL, "invalid or freed container");
   if (!x || !y) return fail(SPECTRA_E_INVAL, "null x or y");
   if ((reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(y) & 3))
     return fail(SPECTRA_E_INVAL, "x and y must be 4-byte aligned");
@@ -588,13 +604,15 @@ int spectra_gemm_grouped(const spectra_container* const* cs, int count, const vo
   if (count < 1 || count > 64) return fail(SPECTRA_E_INVAL, "count out of range [1, 64]");
   if (M != 1) return fail(SPECTRA_E_UNSUPPORTED, "grouped launch supports M = 1");
   DeviceView vs[64];
+  const spectra_container* objs[64];
   for (int i = 0; i < count; ++i) {
-    if (!live(cs[i])) return fail(SPECTRA_E_INVAL, "invalid or freed container in group");
+    objs[i] = cont(cs[i]);
+    if (!objs[i]) return fail(SPECTRA_E_INVAL, "invalid or freed container in group");
     if (!ys[i] || (reinterpret_cast<uintptr_t>(ys[i]) & 3))
       return fail(SPECTRA_E_INVAL, "null or misaligned y in group");
-    if (cs[i]->K != cs[0]->K || cs[i]->device != cs[0]->device)
+    if (objs[i]->K != objs[0]->K || objs[i]->device != objs[0]->device)
       return fail(SPECTRA_E_INVAL, "grouped containers must share K and device");
-    vs[i] = cs[i]->view();
+    vs[i] = objs[i]->view();
     if (!gemv_supports(vs[i], 1))
       return fail(SPECTRA_E_UNSUPPORTED, "GEMV kernel cannot run a container of the group");
   }
@@ -607,8 +625,9 @@ int spectra_gemm_grouped(const spectra_container* const* cs, int count, const vo
   return SPECTRA_OK;
 }
 
-int spectra_embed(const spectra_container* c, const void* ids, int64_t T, void* out, void* stream) {
-  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+int spectra_embed(const spectra_container* h, const void* ids, int64_t T, void* out, void* stream) {
+  const spectra_container* c = cont(h);
+  if (!c) return fail(SPECTRA_E_INVAL, "invalid or freed container");
   if (T < 0 || T > SPECTRA_MAX_T) return fail(SPECTRA_E_INVAL, "T out of range [0, 2^31]");
   if (T == 0) return SPECTRA_OK;
   if (!ids || !out) return fail(SPECTRA_E_INVAL, "null ids or out");
@@ -630,7 +649,7 @@ int spectra_validate_image(const void* image, uint64_t bytes) {
 
 spectra_container* spectra_import(const void* image, uint64_t bytes) {
   if (!image) {
-    set_error("null image");
+    set_error("null image", SPECTRA_E_INVAL);
     return nullptr;
   }
   ImageFields f;
@@ -640,15 +659,15 @@ spectra_container* spectra_import(const void* image, uint64_t bytes) {
   const hipError_t e = hipMemcpy(c->dev, image, bytes, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     drop_container(c);
-    set_error(hip_msg("upload of the image", e));
+    set_error(hip_msg("upload of the image", e), SPECTRA_E_HIP);
     return nullptr;
   }
-  register_handle(c);
-  return c;
+  return containers().publish(c);
 }
 
-int spectra_save(const spectra_container* c, const char* path, uint64_t chunk_bytes) {
-  if (!live(c)) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+int spectra_save(const spectra_container* h, const char* path, uint64_t chunk_bytes) {
+  const spectra_container* c = cont(h);
+  if (!c) return fail(SPECTRA_E_INVAL, "invalid or freed container");
   if (!path) return fail(SPECTRA_E_INVAL, "null path");
   const uint64_t chunk = chunk_size(chunk_bytes);
   Pinned stage;
@@ -675,30 +694,30 @@ int spectra_save(const spectra_container* c, const char* path, uint64_t chunk_by
 
 spectra_container* spectra_load(const char* path, uint64_t chunk_bytes) {
   if (!path) {
-    set_error("null path");
+    set_error("null path", SPECTRA_E_INVAL);
     return nullptr;
   }
   File in;
   in.fp = fopen(path, "rb");
   if (!in.fp) {
-    set_error(std::string("cannot open ") + path);
+    set_error(std::string("cannot open ") + path, SPECTRA_E_IO);
     return nullptr;
   }
   struct stat sb;
   if (fstat(fileno(in.fp), &sb) != 0 || sb.st_size < 0) {
-    set_error(std::string("cannot stat ") + path);
+    set_error(std::string("cannot stat ") + path, SPECTRA_E_IO);
     return nullptr;
   }
   const uint64_t bytes = (uint64_t)sb.st_size;
   unsigned char hdr[kHeaderBytes];
   if (bytes < kHeaderBytes || fread(hdr, 1, kHeaderBytes, in.fp) != kHeaderBytes) {
-    set_error(std::string(path) + ": shorter than a container header");
+    set_error(std::string(path) + ": shorter than a container header", SPECTRA_E_INVAL);
     return nullptr;
   }
   ImageFields f;
   if (parse_header(hdr, bytes, f) != SPECTRA_OK) return nullptr;
   if (fseek(in.fp, 0, SEEK_SET) != 0) {
-    set_error(std::string("cannot rewind ") + path);
+    set_error(std::string("cannot rewind ") + path, SPECTRA_E_IO);
     return nullptr;
   }
   const uint64_t chunk = chunk_size(chunk_bytes);
@@ -706,13 +725,13 @@ spectra_container* spectra_load(const char* path, uint64_t chunk_bytes) {
   for (int i = 0; i < 2; ++i) {
     const hipError_t e = hipHostMalloc(&stage[i].p, chunk, hipHostMallocDefault);
     if (e != hipSuccess) {
-      set_error(hip_msg("pinned staging buffer", e));
+      set_error(hip_msg("pinned staging buffer", e), SPECTRA_E_NOMEM);
       return nullptr;
     }
   }
   hipStream_t s = nullptr;
   if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
-    set_error("stream creation failed");
+    set_error("stream creation failed", SPECTRA_E_HIP);
     return nullptr;
   }
   hipEvent_t done[2] = {nullptr, nullptr};
@@ -761,19 +780,18 @@ spectra_container* spectra_load(const char* path, uint64_t chunk_bytes) {
     drop_container(c);
     return nullptr;
   }
-  register_handle(c);
-  return c;
+  return containers().publish(c);
 }
 
 spectra_kv* spectra_kv_create(int64_t capacity, int32_t heads, int32_t head_dim) {
   if (capacity < 1 || capacity > ((int64_t)1 << 31) || !kv_shape_supported(heads, head_dim)) {
-    set_error("KV cache: capacity in [1, 2^31], heads in [1, 1024], head_dim 64, 128 or 256");
+    set_error("KV cache: capacity in [1, 2^31], heads in [1, 1024], head_dim 64, 128 or 256", SPECTRA_E_INVAL);
     return nullptr;
   }
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) {
-    set_error(hip_msg("hipGetDevice", e));
+    set_error(hip_msg("hipGetDevice", e), SPECTRA_E_HIP);
     return nullptr;
   }
   const uint64_t G = (uint64_t)head_dim / 32;
@@ -781,14 +799,14 @@ spectra_kv* spectra_kv_create(int64_t capacity, int32_t heads, int32_t head_dim)
   const uint64_t rec = align_up(16 * n), sc = align_up(2 * n), zb = align_up(n / 2);
   spectra_kv* kv = new (std::nothrow) spectra_kv();
   if (!kv) {
-    set_error("host allocation of the KV handle failed");
+    set_error("host allocation of the KV handle failed", SPECTRA_E_NOMEM);
     return nullptr;
   }
   void* p = nullptr;
   e = hipMalloc(&p, 2 * (rec + sc + zb));
   if (e != hipSuccess) {
     delete kv;
-    set_error(hip_msg("hipMalloc (KV cache)", e));
+    set_error(hip_msg("hipMalloc (KV cache)", e), SPECTRA_E_NOMEM);
     return nullptr;
   }
   unsigned char* b = static_cast<unsigned char*>(p);
@@ -810,14 +828,12 @@ spectra_kv* spectra_kv_create(int64_t capacity, int32_t heads, int32_t head_dim)
   v.H = heads;
   v.D = head_dim;
   v.G = (int32_t)G;
-  KvRegistry& r = kv_registry();
-  std::lock_guard<std::mutex> lk(r.mu);
-  r.live.insert(kv);
-  return kv;
+  return kvs().publish(kv);
 }
 
-int spectra_kv_append(spectra_kv* kv, const void* k, const void* v, int64_t T, void* stream) {
-  if (!kv_live(kv)) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
+int spectra_kv_append(spectra_kv* h, const void* k, const void* v, int64_t T, void* stream) {
+  spectra_kv* kv = kvs().get(h);
+  if (!kv) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
   if (T < 0) return fail(SPECTRA_E_INVAL, "T < 0");
   if (T > kv->view.cap - kv->length) return fail(SPECTRA_E_INVAL, "append past the KV cache capacity");
   if (T == 0) return SPECTRA_OK;
@@ -831,8 +847,9 @@ int spectra_kv_append(spectra_kv* kv, const void* k, const void* v, int64_t T, v
   return SPECTRA_OK;
 }
 
-int spectra_kv_attend(const spectra_kv* kv, const void* q, int32_t q_heads, void* out, void* stream) {
-  if (!kv_live(kv)) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
+int spectra_kv_attend(const spectra_kv* h, const void* q, int32_t q_heads, void* out, void* stream) {
+  const spectra_kv* kv = kvs().get(h);
+  if (!kv) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
   if (kv->length < 1) return fail(SPECTRA_E_INVAL, "attention over an empty KV cache");
   if (kv->length > kv_max_attend_length())
     return fail(SPECTRA_E_UNSUPPORTED, "attention over more than 524288 cached tokens");
@@ -853,16 +870,21 @@ int spectra_kv_attend(const spectra_kv* kv, const void* q, int32_t q_heads, void
   return SPECTRA_OK;
 }
 
-int64_t spectra_kv_length(const spectra_kv* kv) { return kv_live(kv) ? kv->length : -1; }
+int64_t spectra_kv_length(const spectra_kv* h) {
+  const spectra_kv* kv = kvs().get(h);
+  return kv ? kv->length : -1;
+}
 
-int spectra_kv_reset(spectra_kv* kv) {
-  if (!kv_live(kv)) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
+int spectra_kv_reset(spectra_kv* h) {
+  spectra_kv* kv = kvs().get(h);
+  if (!kv) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
   kv->length = 0;
   return SPECTRA_OK;
 }
 
-int spectra_kv_export(const spectra_kv* kv, void* host_dst, uint64_t cap) {
-  if (!kv_live(kv)) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
+int spectra_kv_export(const spectra_kv* h, void* host_dst, uint64_t cap) {
+  const spectra_kv* kv = kvs().get(h);
+  if (!kv) return fail(SPECTRA_E_INVAL, "invalid or freed KV cache");
   if (!host_dst) return fail(SPECTRA_E_INVAL, "null destination");
   const uint64_t n = (uint64_t)kv->length * (uint64_t)kv->view.H * (uint64_t)kv->view.G;
   const uint64_t part[3] = {16 * n, 2 * n, n / 2};
@@ -881,18 +903,112 @@ int spectra_kv_export(const spectra_kv* kv, void* host_dst, uint64_t cap) {
   return SPECTRA_OK;
 }
 
-void spectra_kv_free(spectra_kv* kv) {
-  {
-    KvRegistry& r = kv_registry();
-    std::lock_guard<std::mutex> lk(r.mu);
-    if (!kv || r.live.erase(kv) == 0) return;
-  }
+void spectra_kv_free(spectra_kv* h) {
+  spectra_kv* kv = kvs().retire(h);
+  if (!kv) return;
   int cur = -1;
   (void)hipGetDevice(&cur);
   if (cur != kv->device) (void)hipSetDevice(kv->device);
   (void)hipFree(kv->dev);
   if (cur >= 0 && cur != kv->device) (void)hipSetDevice(cur);
   delete kv;
+}
+
+spectra_step* spectra_step_create(const spectra_step_phase* phases, int32_t nphases) {
+  set_error("", SPECTRA_E_INVAL);
+  if (!phases) {
+    set_error("null phases", SPECTRA_E_INVAL);
+    return nullptr;
+  }
+  if (nphases < 1 || nphases > 4096) {
+    set_error("phase count out of range [1, 4096]", SPECTRA_E_INVAL);
+    return nullptr;
+  }
+  std::vector<StepPhaseSpec> spec((size_t)nphases);
+  int device = -1;
+  for (int p = 0; p < nphases; ++p) {
+    const spectra_step_phase& ph = phases[p];
+    StepPhaseSpec& sp = spec[(size_t)p];
+    if (ph.ntasks < 1 || ph.ntasks > SPECTRA_STEP_MAX_TASKS) {
+      set_error("tasks per phase out of range [1, 4]", SPECTRA_E_INVAL);
+      return nullptr;
+    }
+    sp.ntasks = ph.ntasks;
+    for (int i = 0; i < ph.ntasks; ++i) {
+      const spectra_container* c = cont(ph.c[i]);
+      if (!c) {
+        set_error("invalid or freed container in a phase", SPECTRA_E_INVAL);
+        return nullptr;
+      }
+      if (device < 0) device = c->device;
+      if (c->device != device) {
+        set_error("the containers of a decode step must share one device", SPECTRA_E_INVAL);
+        return nullptr;
+      }
+      sp.t[i].v = c->view();
+      sp.t[i].y = static_cast<uint16_t*>(ph.y[i]);
+    }
+    if (ph.input < -1 || ph.input >= p) {
+      set_error("a phase's input must be -1 (external x) or an earlier phase", SPECTRA_E_INVAL);
+      return nullptr;
+    }
+    sp.input = ph.input;
+    sp.x = static_cast<const uint16_t*>(ph.x);
+    sp.x_scale = ph.x_scale;
+  }
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  if (cur != device && hipSetDevice(device) != hipSuccess) {
+    set_error("cannot make the containers' device current", SPECTRA_E_HIP);
+    return nullptr;
+  }
+  StepPlan* plan = nullptr;
+  const int st = step_plan_create(spec.data(), nphases, device, &plan);
+  if (cur >= 0 && cur != device) (void)hipSetDevice(cur);
+  if (st != SPECTRA_OK) return nullptr;
+  spectra_step* obj = new (std::nothrow) spectra_step();
+  if (!obj) {
+    step_plan_free(plan);
+    set_error("host allocation of the step handle failed", SPECTRA_E_NOMEM);
+    return nullptr;
+  }
+  obj->plan = plan;
+  return steps().publish(obj);
+}
+
+int spectra_step_run(spectra_step* h, void* stream) {
+  spectra_step* st = steps().get(h);
+  if (!st) return fail(SPECTRA_E_INVAL, "invalid or freed decode step");
+  const hipError_t e = step_plan_run(st->plan, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("decode step launch", e));
+  return SPECTRA_OK;
+}
+
+int spectra_step_status(spectra_step* h, void* stream) {
+  spectra_step* st = steps().get(h);
+  if (!st) return fail(SPECTRA_E_INVAL, "invalid or freed decode step");
+  const int r = step_plan_check(st->plan, static_cast<hipStream_t>(stream));
+  if (r < 0) return r;
+  if (r > 0) return fail(SPECTRA_E_TIMEOUT, "a wait inside the decode step gave up; its outputs are invalid");
+  return SPECTRA_OK;
+}
+
+int spectra_step_test_hooks(spectra_step* h, uint32_t poll_limit, uint32_t tag_skew) {
+  spectra_step* st = steps().get(h);
+  if (!st) return fail(SPECTRA_E_INVAL, "invalid or freed decode step");
+  return step_plan_test_hooks(st->plan, poll_limit, tag_skew);
+}
+
+void spectra_step_free(spectra_step* h) {
+  spectra_step* st = steps().retire(h);
+  if (!st) return;
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  const int dev = step_plan_device(st->plan);
+  if (cur != dev) (void)hipSetDevice(dev);
+  step_plan_free(st->plan);
+  if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+  delete st;
 }
 
 }  // extern "C"

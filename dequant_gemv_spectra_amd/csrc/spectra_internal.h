@@ -90,7 +90,8 @@ struct spectra_container {
 
 namespace spectra {
 
-void set_error(const std::string& msg);
+// Records the latest failure of the calling thread (status SPECTRA_OK for "").
+void set_error(const std::string& msg, int status);
 int fail(int status, const std::string& msg);
 
 // ---- packer (pack.hip) ----
@@ -142,6 +143,66 @@ hipError_t launch_kv_append(const KvView& c, const uint16_t* k, const uint16_t* 
                             hipStream_t s);
 hipError_t launch_kv_attend(const KvView& c, const uint16_t* q, int rep, int64_t L, uint16_t* out, void* ws,
                             hipStream_t s);
+
+// ---- persistent decode step (step.hip) ----
+constexpr int kStepMaxTasks = 4;
+// One container of a phase, as the kernel reads it (device table).
+struct StepTaskDev {
+  const uint4* codes;
+  const uint16_t* scales;
+  const uint8_t* zeros;
+  const uint16_t* outliers;
+  const int32_t* perm;
+  uint16_t* y;        // plain fp16 output [N]
+  uint32_t* ytag;     // tagged copy (tag << 16 | fp16) when a later phase reads it, else null
+  int32_t N, K, K_b, G, n_out;
+  int32_t first_block, rows_per_block, ntiles;
+};
+struct StepPhaseDev {
+  const uint16_t* x;     // external input [K], or null
+  const uint32_t* xtag;  // tagged input (an earlier phase's output), or null
+  float x_scale;         // power of two applied to x as it is staged
+  int32_t ntasks;
+  int32_t lg, P;         // log2 of lanes per row, group slots per lane
+  int32_t pad[2];
+  StepTaskDev t[kStepMaxTasks];
+};
+// Control words of one plan (device memory, zeroed at creation and after an error).
+struct StepCtl {
+  uint32_t seq;          // launches completed (the tag of a launch is 1 + seq % 65535)
+  uint32_t pad0[63];
+  uint32_t done;         // blocks finished, cumulative over launches
+  uint32_t pad1[63];
+  uint32_t err;          // bit 0: a wait gave up
+  uint32_t poll_limit;   // 0: the built-in limit; testing hook
+  uint32_t tag_skew;     // added to the tag consumers expect; testing hook (0 in use)
+  uint32_t pad2[61];
+};
+struct StepTaskSpec {
+  DeviceView v;
+  uint16_t* y;
+};
+struct StepPhaseSpec {
+  int ntasks;
+  StepTaskSpec t[kStepMaxTasks];
+  int input;             // -1: external x; else an earlier phase whose task 0 output is the input
+  const uint16_t* x;
+  float x_scale;
+};
+struct StepPlan;
+// Builds the plan (device table, control words, tag buffers); status < 0 with
+// the error set on failure.
+int step_plan_create(const StepPhaseSpec* ph, int nph, int device, StepPlan** out);
+hipError_t step_plan_run(StepPlan* p, hipStream_t s);
+// Waits for s, reads the error word; on an error clears the plan's control
+// words and tags and returns 1.  < 0: a HIP call failed.
+int step_plan_check(StepPlan* p, hipStream_t s);
+int step_plan_test_hooks(StepPlan* p, uint32_t poll_limit, uint32_t tag_skew);
+int step_plan_device(const StepPlan* p);
+void step_plan_free(StepPlan* p);
+// Lanes per row and group slots per lane of the M = 1 GEMV for G groups per
+// row (false: no variant runs G).
+bool gemv_variant(int G, int* L, int* P);
 
 // ---- per-stream workspace (abi.hip) ----
 // A device buffer of at least `bytes` reserved for work enqueued on stream s

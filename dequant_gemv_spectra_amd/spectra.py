@@ -21,6 +21,7 @@ SPECTRA_E_NOMEM = -3
 SPECTRA_E_HIP = -4
 SPECTRA_E_UNSUPPORTED = -5
 SPECTRA_E_IO = -6
+SPECTRA_E_TIMEOUT = -7
 
 KERNELS = {"auto": 0, "gemv": 1, "mfma": 2}
 
@@ -29,13 +30,23 @@ EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm
             "spectra_export", "spectra_validate_image", "spectra_import", "spectra_save",
             "spectra_load", "spectra_kv_create", "spectra_kv_append", "spectra_kv_attend",
             "spectra_kv_length", "spectra_kv_reset", "spectra_kv_export", "spectra_kv_free",
-            "spectra_last_error", "spectra_version"]
+            "spectra_step_create", "spectra_step_run", "spectra_step_status", "spectra_step_test_hooks",
+            "spectra_step_free", "spectra_last_error", "spectra_last_status", "spectra_version"]
 
 
 class SpectraError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"spectra status {status}: {msg}")
         self.status = status
+
+
+STEP_MAX_TASKS = 4
+
+
+class spectra_step_phase(ctypes.Structure):
+    _fields_ = [("ntasks", ctypes.c_int32), ("c", ctypes.c_void_p * STEP_MAX_TASKS),
+                ("y", ctypes.c_void_p * STEP_MAX_TASKS), ("input", ctypes.c_int32),
+                ("x", ctypes.c_void_p), ("x_scale", ctypes.c_float)]
 
 
 class spectra_info_t(ctypes.Structure):
@@ -102,8 +113,20 @@ def lib() -> ctypes.CDLL:
     L.spectra_info.restype = c_int
     L.spectra_export.argtypes = [vp, vp, u64]
     L.spectra_export.restype = c_int
+    L.spectra_step_create.argtypes = [ctypes.POINTER(spectra_step_phase), ctypes.c_int32]
+    L.spectra_step_create.restype = vp
+    L.spectra_step_run.argtypes = [vp, vp]
+    L.spectra_step_run.restype = c_int
+    L.spectra_step_status.argtypes = [vp, vp]
+    L.spectra_step_status.restype = c_int
+    L.spectra_step_test_hooks.argtypes = [vp, ctypes.c_uint32, ctypes.c_uint32]
+    L.spectra_step_test_hooks.restype = c_int
+    L.spectra_step_free.argtypes = [vp]
+    L.spectra_step_free.restype = None
     L.spectra_last_error.argtypes = []
     L.spectra_last_error.restype = ctypes.c_char_p
+    L.spectra_last_status.argtypes = []
+    L.spectra_last_status.restype = c_int
     L.spectra_version.argtypes = []
     L.spectra_version.restype = c_int
     _lib = L
@@ -112,6 +135,16 @@ def lib() -> ctypes.CDLL:
 
 def spectra_last_error() -> str:
     return lib().spectra_last_error().decode()
+
+
+def spectra_last_status() -> int:
+    return lib().spectra_last_status()
+
+
+def _null_handle_error() -> "SpectraError":
+    """The error behind a NULL handle, classified by the library's status code."""
+    st = spectra_last_status()
+    return SpectraError(st if st < 0 else SPECTRA_E_INVAL, spectra_last_error())
 
 
 def _check(status: int):
@@ -188,9 +221,7 @@ def spectra_pack(W, gamma, stream=None) -> Container:
         p = lib().spectra_pack_device(ctypes.c_void_p(W.data_ptr()), ctypes.c_void_p(gamma.data_ptr()),
                                       K, N, _stream_ptr(stream))
     if not p:
-        msg = spectra_last_error()
-        status = SPECTRA_E_NONFINITE if "non-finite" in msg else SPECTRA_E_INVAL
-        raise SpectraError(status, msg)
+        raise _null_handle_error()
     return Container(p)
 
 
@@ -253,14 +284,6 @@ def spectra_embed(c: Container, ids, out=None, stream=None):
     return out
 
 
-def _status_of(msg: str) -> int:
-    if msg.startswith("cannot ") or "read of" in msg or "write to" in msg:
-        return SPECTRA_E_IO
-    if "hipMalloc" in msg or "pinned" in msg:
-        return SPECTRA_E_NOMEM
-    return SPECTRA_E_INVAL
-
-
 def spectra_validate_image(image: bytes) -> None:
     """Raise SpectraError unless `image` is a well-formed container image."""
     buf = (ctypes.c_ubyte * len(image)).from_buffer_copy(image) if image else None
@@ -272,8 +295,7 @@ def spectra_import(image: bytes) -> Container:
     buf = (ctypes.c_ubyte * len(image)).from_buffer_copy(image) if image else None
     p = lib().spectra_import(buf, len(image))
     if not p:
-        msg = spectra_last_error()
-        raise SpectraError(_status_of(msg), msg)
+        raise _null_handle_error()
     return Container(p)
 
 
@@ -285,8 +307,7 @@ def spectra_load(path: str, chunk_bytes: int = 0) -> Container:
     """Stream a container file into a new container on the current device."""
     p = lib().spectra_load(os.fsencode(path), chunk_bytes)
     if not p:
-        msg = spectra_last_error()
-        raise SpectraError(_status_of(msg), msg)
+        raise _null_handle_error()
     return Container(p)
 
 
@@ -296,7 +317,7 @@ class KvCache:
     def __init__(self, capacity: int, heads: int, head_dim: int):
         p = lib().spectra_kv_create(capacity, heads, head_dim)
         if not p:
-            raise SpectraError(SPECTRA_E_INVAL, spectra_last_error())
+            raise _null_handle_error()
         self.handle = ctypes.c_void_p(p)
         self.heads, self.head_dim = heads, head_dim
 
@@ -339,6 +360,67 @@ class KvCache:
     def close(self) -> None:
         if self.handle:
             lib().spectra_kv_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class StepPlan:
+    """Owning handle of a decode step: a chain of dependent M = 1 products run
+    by one persistent launch (spectra_step_create).
+
+    phases: sequence of dicts with keys
+      "containers": 1 .. 4 Containers sharing K,
+      "ys": matching CUDA fp16 output tensors [N_i] (or [1][N_i]),
+      "input": -1 for an external x, else the index of an earlier phase whose
+               first container's output is the input,
+      "x": CUDA fp16 [K] tensor when input == -1,
+      "x_scale": power of two applied to the staged input (default 1.0).
+    The plan borrows the containers and tensors; keep them alive while it is used.
+    """
+
+    def __init__(self, phases):
+        n = len(phases)
+        arr = (spectra_step_phase * n)()
+        self._keep = []
+        for i, ph in enumerate(phases):
+            cs, ys = list(ph["containers"]), list(ph["ys"])
+            if not 1 <= len(cs) <= STEP_MAX_TASKS or len(ys) != len(cs):
+                raise ValueError("each phase needs 1 .. 4 containers and as many outputs")
+            arr[i].ntasks = len(cs)
+            for j, (c, y) in enumerate(zip(cs, ys)):
+                arr[i].c[j] = c.handle.value
+                arr[i].y[j] = y.data_ptr()
+            arr[i].input = int(ph.get("input", -1))
+            x = ph.get("x")
+            arr[i].x = x.data_ptr() if x is not None else None
+            arr[i].x_scale = float(ph.get("x_scale", 1.0))
+            self._keep.append((cs, ys, x))
+        p = lib().spectra_step_create(arr, n)
+        if not p:
+            raise _null_handle_error()
+        self.handle = ctypes.c_void_p(p)
+
+    def run(self, stream=None) -> None:
+        _check(lib().spectra_step_run(self.handle, _stream_ptr(stream)))
+
+    def status(self, stream=None) -> int:
+        """SPECTRA_OK, or SPECTRA_E_TIMEOUT when a wait of an earlier run gave up."""
+        st = lib().spectra_step_status(self.handle, _stream_ptr(stream))
+        if st not in (SPECTRA_OK, SPECTRA_E_TIMEOUT):
+            _check(st)
+        return st
+
+    def test_hooks(self, poll_limit: int = 0, tag_skew: int = 0) -> None:
+        _check(lib().spectra_step_test_hooks(self.handle, poll_limit, tag_skew))
+
+    def close(self) -> None:
+        if self.handle:
+            lib().spectra_step_free(self.handle)
             self.handle = None
 
     def __del__(self):

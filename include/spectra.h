@@ -89,6 +89,9 @@
  *  - Functions returning int return SPECTRA_OK or a negative spectra_status.
  *    No exception or abort crosses the ABI.  spectra_last_error() returns a
  *    thread-local message describing the latest failure on the calling thread.
+ *  - Handles (spectra_container*, spectra_kv*, spectra_step*) are opaque
+ *    identifiers, never reissued: a freed handle stays invalid for the life of
+ *    the process, and every call checks its handle before using it.
  *  - A container owns one device allocation on the device that was current
  *    when it was packed; it is immutable after packing and may be used by
  *    concurrent spectra_gemm* calls on any streams of that device.
@@ -114,7 +117,8 @@ typedef enum {
   SPECTRA_E_NOMEM = -3,        /* a device or host allocation failed */
   SPECTRA_E_HIP = -4,          /* a HIP runtime call failed (message has the HIP error string) */
   SPECTRA_E_UNSUPPORTED = -5,  /* the forced kernel cannot run this shape */
-  SPECTRA_E_IO = -6            /* a file could not be opened, read or written */
+  SPECTRA_E_IO = -6,           /* a file could not be opened, read or written */
+  SPECTRA_E_TIMEOUT = -7       /* a bounded wait inside a decode step gave up (its outputs are invalid) */
 } spectra_status;
 
 /* Kernel selection for spectra_gemm_ex. */
@@ -214,6 +218,69 @@ int spectra_gemm_grouped(const spectra_container* const* cs, int count, const vo
 int spectra_embed(const spectra_container* c, const void* ids, int64_t T, void* out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Decode step: a chain of dependent M = 1 products in one launch.
+ *
+ * At decode every token streams all weights once and the projections of a
+ * layer depend on one another (SPECTRA page, abstract: its fused kernels run
+ * under graph replay to cut per-launch overhead; techfi24 summary, section on
+ * the hardware context: decode is bound by weight bytes).  A step is a list
+ * of phases; phase p computes y_i = x_p W_hat_i^T (as spectra_gemm with
+ * M = 1, bit for bit the GEMV's result) for its 1 .. 4 containers, which share
+ * K.  Its input x_p is either an external DEVICE fp16 [K] vector or the output
+ * of task 0 of an earlier phase q (then K must equal that container's N), and
+ * it is staged as fp16(x * x_scale) with x_scale a power of two in
+ * [2^-24, 2^24] (exact; 1 leaves x unchanged).  One launch runs every phase
+ * in order with one persistent block per compute unit: a phase starts its
+ * arithmetic once the output it reads is complete, while the blocks already
+ * stream its weights.
+ *
+ * Ownership: the plan borrows the containers and the x and y buffers, which
+ * must stay valid until spectra_step_free; it owns a small device allocation
+ * (control words, phase table and a 4-byte tagged copy of each output that a
+ * later phase reads).  Runs of one plan must not overlap (one stream, or
+ * ordered streams); plans are independent of one another.  Each wait inside
+ * the kernel is bounded: a wait that gives up marks the plan and the kernel
+ * still completes; spectra_step_status reports it.
+ * Limits: K <= 16384, at most 320 groups per row (G), at most 4 heavy-tailed
+ * channels per lane of the GEMV mapping (n_out <= 64 for G <= 80, 128 for
+ * G <= 160, 256 otherwise), and the staging of the largest phase within the
+ * LDS of one block (E_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------- */
+typedef struct spectra_step spectra_step;
+
+#define SPECTRA_STEP_MAX_TASKS 4
+
+typedef struct {
+  int32_t ntasks;                                   /* 1 .. SPECTRA_STEP_MAX_TASKS */
+  const spectra_container* c[SPECTRA_STEP_MAX_TASKS];
+  void* y[SPECTRA_STEP_MAX_TASKS];                  /* DEVICE fp16 [N_i] outputs, 2-byte aligned */
+  int32_t input;                                    /* -1: x below; else an earlier phase index */
+  const void* x;                                    /* DEVICE fp16 [K], 4-byte aligned, when input == -1 */
+  float x_scale;                                    /* power of two applied to the staged input */
+} spectra_step_phase;
+
+/* Validates the phases and builds the plan on the containers' device.  NULL
+ * on error (E_INVAL, E_UNSUPPORTED, E_NOMEM, E_HIP; see spectra_last_error). */
+spectra_step* spectra_step_create(const spectra_step_phase* phases, int32_t nphases);
+
+/* Enqueues one run of every phase on `stream` (NULL = null stream); returns
+ * at once.  May be captured into a HIP graph and replayed. */
+int spectra_step_run(spectra_step* st, void* stream);
+
+/* Waits for `stream`, then reports whether a wait of an earlier run gave up:
+ * SPECTRA_OK, or SPECTRA_E_TIMEOUT (the plan's control state is then reset,
+ * so the next run starts clean). */
+int spectra_step_status(spectra_step* st, void* stream);
+
+/* Testing the bounded waits: poll_limit (0 = built-in) caps each wait's
+ * polls, and tag_skew != 0 makes every wait expect a mark no producer
+ * writes, so each wait gives up after poll_limit polls.  Synchronous. */
+int spectra_step_test_hooks(spectra_step* st, uint32_t poll_limit, uint32_t tag_skew);
+
+/* Releases the plan's device memory.  NULL-safe; unknown handles are ignored. */
+void spectra_step_free(spectra_step* st);
+
+/* ---------------------------------------------------------------------------
  * Group-32 4-bit KV cache (SPECTRA page, abstract: the key-value cache is kept
  * in microscaled Group-32 4-bit form).  One cache holds the keys and values of
  * one attention layer for up to `capacity` tokens, `heads` cache heads of
@@ -264,9 +331,8 @@ int spectra_kv_export(const spectra_kv* kv, void* host_dst, uint64_t cap);
 void spectra_kv_free(spectra_kv* kv);
 
 /* Release the container and its device memory.  NULL-safe; freeing a handle
- * twice, or one this library did not return, does nothing.  Handles are
- * checked against the library's set of live containers, so any later call
- * with a freed handle returns SPECTRA_E_INVAL without dereferencing it. */
+ * twice, or one this library did not return, does nothing.  Any later call
+ * with a freed handle returns SPECTRA_E_INVAL (handles are never reissued). */
 void spectra_free(spectra_container* c);
 
 /* Shape and byte counts of a container. */
@@ -316,6 +382,11 @@ spectra_container* spectra_load(const char* path, uint64_t chunk_bytes);
 
 /* Thread-local description of the latest error on the calling thread ("" if none). */
 const char* spectra_last_error(void);
+
+/* Status code (a negative spectra_status) of that latest error, SPECTRA_OK if
+ * none: how a caller classifies the failure of an entry point that returns a
+ * NULL handle (spectra_pack, spectra_import, spectra_load, ...). */
+int spectra_last_status(void);
 
 /* ABI version (1). */
 int spectra_version(void);
