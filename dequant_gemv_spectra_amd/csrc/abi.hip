@@ -65,9 +65,16 @@ const DeviceProps& device_props(int device) {
 }
 
 namespace {
+// Per (device, stream) workspaces.  A buffer that is outgrown is retired, not
+// freed: a HIP graph captured earlier on that stream may still hold its
+// address and be replayed later.  Retired buffers are freed only by
+// spectra_release_workspaces, which the caller invokes once no such graph
+// will run again (the total retired is below the live size, since each
+// growth at least doubles it).
 struct WorkspaceCache {
   std::mutex mu;
   std::map<std::pair<int, void*>, std::pair<void*, size_t>> bufs;
+  std::vector<std::pair<int, void*>> retired;  // (device, buffer)
 };
 WorkspaceCache& workspace_cache() {
   static WorkspaceCache wc;
@@ -83,19 +90,30 @@ hipError_t stream_workspace(int device, hipStream_t s, size_t bytes, void** out)
     *out = e.first;
     return hipSuccess;
   }
-  hipError_t err;
-  if (e.first) {  // work already queued on s may still read the old buffer
-    if ((err = hipStreamSynchronize(s)) != hipSuccess) return err;
-    (void)hipFree(e.first);
-    e = std::make_pair(nullptr, (size_t)0);
-  }
   size_t nb = bytes < 2 * e.second ? 2 * e.second : bytes;
   if (nb < (1u << 20)) nb = 1u << 20;
   void* p = nullptr;
-  if ((err = hipMalloc(&p, nb)) != hipSuccess) return err;
+  const hipError_t err = hipMalloc(&p, nb);
+  if (err != hipSuccess) return err;
+  if (e.first) wc.retired.emplace_back(device, e.first);  // work or graphs on s may still use it
   e = std::make_pair(p, nb);
   *out = p;
   return hipSuccess;
+}
+
+int release_workspaces() {
+  WorkspaceCache& wc = workspace_cache();
+  std::lock_guard<std::mutex> lk(wc.mu);
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  int st = SPECTRA_OK;
+  for (const auto& r : wc.retired) {
+    if (hipSetDevice(r.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess || hipFree(r.second) != hipSuccess)
+      st = SPECTRA_E_HIP;
+  }
+  wc.retired.clear();
+  if (cur >= 0) (void)hipSetDevice(cur);
+  return st;
 }
 
 namespace {
@@ -454,6 +472,12 @@ int spectra_version(void) { return 1; }
 const char* spectra_last_error(void) { return g_last_error.c_str(); }
 
 int spectra_last_status(void) { return g_last_status; }
+
+int spectra_release_workspaces(void) {
+  const int st = release_workspaces();
+  if (st != SPECTRA_OK) return fail(st, "freeing a retired workspace failed");
+  return SPECTRA_OK;
+}
 
 spectra_container* spectra_pack_device(const void* W, const void* gamma, int64_t K, int64_t N,
                                        void* stream) {

@@ -1,5 +1,6 @@
 // Group-32 quantizer helpers shared by the weight packer and the KV-cache
-// append kernel (device code of libspectra only).
+// append kernel.  Also compiled for the host, so that a CPU test can check the
+// conversion against numpy on every binary16 value and rounding midpoint.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,7 +8,7 @@
 
 namespace spectra {
 
-__device__ __forceinline__ double g32_h2d(uint16_t b) {
+__host__ __device__ __forceinline__ double g32_h2d(uint16_t b) {
   return (double)__builtin_bit_cast(_Float16, b);
 }
 
@@ -15,7 +16,7 @@ __device__ __forceinline__ double g32_h2d(uint16_t b) {
 // 754 formats: keep 11 significant bits (fewer in the subnormal range, whose
 // unit is 2^-24), round on the dropped bits, let a carry ripple into the
 // exponent field, saturate to infinity past the largest finite value.
-__device__ inline uint16_t f64_to_f16_rne(double v) {
+__host__ __device__ inline uint16_t f64_to_f16_rne(double v) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
   const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
   const int ex = (int)((b >> 52) & 0x7FF);
@@ -47,7 +48,7 @@ __device__ inline uint16_t f64_to_f16_rne(double v) {
 }
 
 // Bit position of member e (0..31) in its code word e / 8.
-__device__ __forceinline__ uint32_t member_shift(int e) {
+__host__ __device__ __forceinline__ uint32_t member_shift(int e) {
   return 16u * (uint32_t)(e & 1) + 4u * (uint32_t)((e & 7) >> 1);
 }
 

@@ -154,11 +154,13 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 //      dequantized from LDS), reduced across the waves -> fp32 partials and
 //      (m, l) per (split, query head).
 // The keys and values of the split are read once for all rep query heads.
+// REP is the build's bound on the query heads per cache head; rep_rt <= REP
+// is the call's (heads past rep_rt score a zero query and write nothing).
 template <int G, int REP>
 __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const uint16_t* __restrict__ q,
                                                          int64_t L, float* __restrict__ part,
-                                                         float* __restrict__ stats) {
-  constexpr int rep = REP;
+                                                         float* __restrict__ stats, const int rep_rt) {
+  const int rep = rep_rt;
   constexpr int D = 32 * G;
   constexpr int NP = D / 2;                   // channel pairs
   constexpr int PL = NP >= 64 ? NP / 64 : 1;  // pairs per lane
@@ -177,9 +179,10 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
   const int H = c.H, Hq = H * rep;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t0 = (int64_t)split * TS;
-  for (int i = threadIdx.x; i < rep * D / 2; i += blockDim.x) {
+  for (int i = threadIdx.x; i < REP * D / 2; i += blockDim.x) {
     const int rr = i / (D / 2), j = i % (D / 2);
-    qs[rr][j] = as_h2(reinterpret_cast<const uint32_t*>(q + (int64_t)(h * rep + rr) * D)[j]);
+    qs[rr][j] = rr < rep ? as_h2(reinterpret_cast<const uint32_t*>(q + (int64_t)(h * rep + rr) * D)[j])
+                         : as_h2(0u);
   }
 
   // 1. the split's value records, scales and zero bytes, a few wide loads per
@@ -316,13 +319,13 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
         }
       }
     __syncthreads();
-    for (int j = threadIdx.x; j < REP * D; j += blockDim.x) {
+    for (int j = threadIdx.x; j < rep * D; j += blockDim.x) {
       const int rr = j / D, d = j % D;
       float sum = 0.f;
       for (int w2 = 0; w2 < WAVES; ++w2) sum += pacc[w2][rr][d];
       part[((int64_t)split * Hq + h * rep + rr) * D + d] = sum;
     }
-    if (threadIdx.x < REP) {
+    if (threadIdx.x < rep) {
       const int64_t base = (int64_t)split * Hq + h * rep + threadIdx.x;
       stats[2 * base] = mst[threadIdx.x];
       stats[2 * base + 1] = lst[threadIdx.x];
@@ -340,12 +343,12 @@ __global__ __launch_bounds__(kPvThreads) void k_kv_split(const KvView c, const u
       }
       __syncthreads();
       const int64_t base = (int64_t)split * Hq + h * rep + rr;
-      for (int d = threadIdx.x; d < D; d += blockDim.x) {
+      for (int d = threadIdx.x; d < D && rr < rep; d += blockDim.x) {
         float sum = 0.f;
         for (int w2 = 0; w2 < WAVES; ++w2) sum += pacc[w2][0][d];
         part[base * D + d] = sum;
       }
-      if (threadIdx.x == 0) {
+      if (threadIdx.x == 0 && rr < rep) {
         stats[2 * base] = mst[rr];
         stats[2 * base + 1] = lst[rr];
       }
@@ -422,14 +425,15 @@ int64_t kv_max_attend_length() { return (int64_t)kMaxSplits * kTokensPerSplit; }
 namespace {
 
 template <int G, int REP>
-hipError_t attend_gr(const KvView& c, const uint16_t* q, int64_t L, uint16_t* out, void* ws, hipStream_t s) {
+hipError_t attend_gr(const KvView& c, const uint16_t* q, int rep, int64_t L, uint16_t* out, void* ws,
+                     hipStream_t s) {
   constexpr int D = 32 * G;
-  const int Hq = c.H * REP;
+  const int Hq = c.H * rep;
   const int64_t splits = splits_of(L);
   float* part = static_cast<float*>(ws);
   float* stats = part + (size_t)splits * Hq * D;
   hipLaunchKernelGGL((k_kv_split<G, REP>), dim3((unsigned)splits, (unsigned)c.H), dim3(kPvThreads), 0, s, c, q, L,
-                     part, stats);
+                     part, stats, rep);
   hipLaunchKernelGGL(k_kv_combine, dim3((unsigned)Hq), dim3(kCombThreads), 0, s, part, stats, (int)splits, Hq, D,
                      out);
   return hipGetLastError();
@@ -438,14 +442,13 @@ hipError_t attend_gr(const KvView& c, const uint16_t* q, int64_t L, uint16_t* ou
 template <int G>
 hipError_t attend_g(const KvView& c, const uint16_t* q, int rep, int64_t L, uint16_t* out, void* ws,
                     hipStream_t s) {
-  switch (rep) {
-    case 1: return attend_gr<G, 1>(c, q, L, out, ws, s);
-    case 2: return attend_gr<G, 2>(c, q, L, out, ws, s);
-    case 4: return attend_gr<G, 4>(c, q, L, out, ws, s);
-    case 8: return attend_gr<G, 8>(c, q, L, out, ws, s);
-    case 16: return attend_gr<G, 16>(c, q, L, out, ws, s);
-    default: return hipErrorNotSupported;
-  }
+  // every ratio 1 .. 16 runs on the build for the next power of two
+  if (rep < 1 || rep > 16) return hipErrorNotSupported;
+  if (rep == 1) return attend_gr<G, 1>(c, q, rep, L, out, ws, s);
+  if (rep == 2) return attend_gr<G, 2>(c, q, rep, L, out, ws, s);
+  if (rep <= 4) return attend_gr<G, 4>(c, q, rep, L, out, ws, s);
+  if (rep <= 8) return attend_gr<G, 8>(c, q, rep, L, out, ws, s);
+  return attend_gr<G, 16>(c, q, rep, L, out, ws, s);
 }
 
 }  // namespace

@@ -67,7 +67,7 @@ constexpr int kSP = 5;              // most group slots per lane
 constexpr int kSOS = 4;             // heavy-tailed slots per lane
 constexpr uint32_t kPollLimit = 1u << 16;
 #ifndef SPECTRA_STEP_PREFETCH
-#define SPECTRA_STEP_PREFETCH 1
+#define SPECTRA_STEP_PREFETCH 0
 #endif
 constexpr int kPrefetch = SPECTRA_STEP_PREFETCH;  // where the next phase's first tiles are requested
 
@@ -366,14 +366,14 @@ __device__ __forceinline__ void gather(const BT& bt, const void* xin, const int3
 }
 
 // The block's tiles of one phase, two register buffers alternating.  On
-// entry fa and fb hold (or have in flight) tiles 0 and 1.  Mode 0: each tile
-// is reloaded right after its compute, the last pair with the next phase's
-// tiles 0 and 1.  Mode 1 (the build's choice): the last pair computes (and
-// stores) both tiles, signals the control wave (B0), then loads the next
-// phase's first tiles, so this block's outputs leave ahead of that burst.
-// Mode 2: no load crosses a phase (the next phase loads its first tiles
-// after its input is staged).  Measured on the 36-layer 4B-class step:
-// 1.69, 1.42 and 1.61 ms.
+// entry fa and fb hold (or have in flight) tiles 0 and 1.  Mode 0 (the
+// build's choice): each tile is reloaded right after its compute, the last
+// pair with the next phase's tiles 0 and 1.  Mode 1: the last pair computes
+// (and stores) both tiles, signals the control wave (B0), then loads the
+// next phase's first tiles, so this block's outputs leave ahead of that
+// burst.  Mode 2: no load crosses a phase (the next phase loads its first
+// tiles after its input is staged).  Measured on the 36-layer 4B-class step:
+// 1.69, 1.78 and 1.83 ms.
 __device__ __forceinline__ void run_phase(Frag& fa, Frag& fb, const BT& cur, const BT& nx, int tid,
                                           const uint16_t* xs, const Nib nb, uint32_t tag) {
   // this lane's P groups of x and its heavy-tailed x, into registers once
@@ -458,7 +458,9 @@ __global__ __launch_bounds__(kStepBlock) void k_step(const StepPhaseDev* __restr
       load_tile(fb, cur, 1, tid);
     }
     for (int p = 0; p < nph; ++p) {
-      if (kPrefetch == 0) bar();  // B0 (modes 1, 2: inside the phase's last tile pair)
+      // B0 (modes 1, 2: the previous phase's last tile pair holds it, so here
+      // only before the first phase)
+      if (kPrefetch == 0 || p == 0) bar();
       bar();  // B1
       gather(cur, xin, perm_lds, xs, tid);
       bar();  // B2

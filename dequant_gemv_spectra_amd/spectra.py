@@ -31,7 +31,8 @@ EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm
             "spectra_load", "spectra_kv_create", "spectra_kv_append", "spectra_kv_attend",
             "spectra_kv_length", "spectra_kv_reset", "spectra_kv_export", "spectra_kv_free",
             "spectra_step_create", "spectra_step_run", "spectra_step_status", "spectra_step_test_hooks",
-            "spectra_step_free", "spectra_last_error", "spectra_last_status", "spectra_version"]
+            "spectra_step_free", "spectra_release_workspaces", "spectra_last_error", "spectra_last_status",
+            "spectra_version"]
 
 
 class SpectraError(RuntimeError):
@@ -125,6 +126,8 @@ def lib() -> ctypes.CDLL:
     L.spectra_step_free.restype = None
     L.spectra_last_error.argtypes = []
     L.spectra_last_error.restype = ctypes.c_char_p
+    L.spectra_release_workspaces.argtypes = []
+    L.spectra_release_workspaces.restype = c_int
     L.spectra_last_status.argtypes = []
     L.spectra_last_status.restype = c_int
     L.spectra_version.argtypes = []
@@ -445,6 +448,12 @@ def spectra_export(c: Container) -> bytes:
     buf = (ctypes.c_ubyte * total)()
     _check(lib().spectra_export(c.handle, buf, total))
     return bytes(buf)
+
+
+def spectra_release_workspaces() -> None:
+    """Free the workspaces earlier growth retired (no graph captured before a
+    growth may be replayed afterwards)."""
+    _check(lib().spectra_release_workspaces())
 
 
 def spectra_version() -> int:

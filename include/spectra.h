@@ -308,8 +308,8 @@ int spectra_kv_append(spectra_kv* kv, const void* k, const void* v, int64_t T, v
  * query head h reading cache head h / (q_heads / heads); K_hat, V_hat are the
  * dequantized cache ((q - z) * s16).  q: DEVICE fp16 [q_heads][head_dim];
  * out: DEVICE fp16 [q_heads][head_dim]; both 4-byte aligned.  q_heads must be
- * a multiple of heads with at most 16 query heads per cache head; length >= 1
- * (E_INVAL otherwise) and at most 524288 (E_UNSUPPORTED).
+ * a multiple of heads with 1 .. 16 query heads per cache head (any ratio);
+ * length >= 1 (E_INVAL otherwise) and at most 524288 (E_UNSUPPORTED).
  * Per element, |out - ref| <= 1e-3 * (sum_t p_t |V_hat[t]|) + 1e-6 with ref
  * and p in binary64.  Uses the per-stream workspace (4 * q_heads *
  * (head_dim + 2) * ceil(length / 128) bytes); enqueued on `stream`. */
@@ -379,6 +379,16 @@ int spectra_save(const spectra_container* c, const char* path, uint64_t chunk_by
  * checked once complete.  Synchronous; NULL on error (E_IO, E_INVAL for a
  * malformed image, E_NOMEM, E_HIP; see spectra_last_error). */
 spectra_container* spectra_load(const char* path, uint64_t chunk_bytes);
+
+/* Device workspaces.  The MFMA path and KV attention use a device workspace
+ * per (device, stream), allocated on first use and grown (to at least twice
+ * its size) when a call needs more.  A grown-out buffer is kept, not freed: a
+ * HIP graph captured earlier on that stream may still hold its address.  The
+ * first call at a new largest size allocates, so make it before a capture.
+ * spectra_release_workspaces synchronizes each device that holds one and
+ * frees every grown-out buffer; call it only when no graph captured before a
+ * growth will be replayed again.  SPECTRA_OK or SPECTRA_E_HIP. */
+int spectra_release_workspaces(void);
 
 /* Thread-local description of the latest error on the calling thread ("" if none). */
 const char* spectra_last_error(void);

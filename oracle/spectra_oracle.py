@@ -35,7 +35,11 @@ Parity status of each function (what pins it, in tests/test_oracle_pins.py):
   outlier_mask       threshold placement via the single-spike closed form
   permutation        invariants (bulk ascending, then flagged ascending)
   quantize_groups    exact round trip of grid-valued groups, all-zero and
-                     one-signed groups, error bound, monotonicity
+                     one-signed groups, error bound, monotonicity; hand-valued
+                     ties: codes and zero points round half to even ({0, 15,
+                     2.5} -> code 2; {-6.5, 8.5} -> z 6, codes 0 and 14), and
+                     so does the fp16 scale (1 + 2^-11 -> 1, 1 + 3*2^-11 ->
+                     1 + 2^-9)
   pack / unpack      hand-written byte fixtures in tests/golden, round trip,
                      footprint closed form, outlier bits
   matmul_ref         pure-Python brute force on tiny shapes, one-hot inputs
@@ -46,7 +50,9 @@ Parity status of each function (what pins it, in tests/test_oracle_pins.py):
   kv_quantize        grid-valued head vectors round-trip exactly; the same
                      groups through quantize_groups directly
   kv_attend_ref      pure-Python brute force (math.exp, explicit sums) on tiny
-                     caches; one-token cache returns V; equal keys average V
+                     caches; one-token cache returns V; equal keys average V;
+                     a two-token cache with hand-computed softmax weights
+  kv_attend_tolerance  the same two-token cache: 1e-3 * p|V| + 1e-6 by hand
 """
 from __future__ import annotations
 

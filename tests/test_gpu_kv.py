@@ -96,6 +96,24 @@ def test_attend_split_boundaries(H, rep, D, L, seed):
     _attend_case(H, rep, D, L, seed)
 
 
+# Every build of the split kernel (rep rounded up to 1, 2, 4, 8, 16) at every
+# head size, at a short cache and one past a split boundary.
+@pytest.mark.parametrize("rep", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("L", [300, 129])
+def test_attend_every_build(rep, D, L):
+    _attend_case(2 if rep < 16 else 1, rep, D, L, 1000 + 10 * rep + D + L)
+
+
+# Ratios that are not powers of two run on the next build with the extra
+# query heads masked: the 1.5B-class layer's 12 query heads over 2 cache heads
+# (6 per cache head), and the other odd ratios.
+@pytest.mark.parametrize("H,rep,D,L", [(2, 6, 128, 700), (1, 3, 64, 200), (3, 5, 128, 129), (2, 7, 256, 300),
+                                       (1, 9, 128, 260), (1, 12, 64, 131), (1, 15, 128, 400)])
+def test_attend_odd_ratios(H, rep, D, L):
+    _attend_case(H, rep, D, L, 2000 + rep)
+
+
 def test_attend_peaked_scores():
     # large keys make the softmax nearly one-hot: the max subtraction matters
     _attend_case(2, 2, 128, 300, 15, k_scale=8.0)

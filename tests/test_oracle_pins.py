@@ -455,3 +455,116 @@ def test_kv_attend_equal_keys_average_values():
     V = rng.standard_normal((L, 1, D))
     q16 = rng.standard_normal((1, D)).astype(np.float16)
     np.testing.assert_allclose(O.kv_attend_ref(q16, K, V)[0], V[:, 0, :].mean(axis=0), rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# rounding ties: codes, zero points and scales round half to even
+# --------------------------------------------------------------------------
+def test_code_and_zero_point_ties_round_half_to_even():
+    # {0, 15, 2.5}: lo = 0, hi = 15, s16 = 1, z = 0; 2.5 is a tie -> code 2
+    # (half up would give 3).  {-6.5, 8.5}: s16 = 1, -lo/s16 = 6.5 is a tie ->
+    # z = 6 (half up: 7); codes rint(-6.5) + 6 = 0 and rint(8.5) + 6 = 14.
+    q, z, s16 = O.quantize_groups(np.array([[0.0, 15.0, 2.5]]))
+    assert float(s16[0, 0]) == 1.0 and int(z[0, 0]) == 0
+    assert list(q[0, 0, :3]) == [0, 15, 2]
+    q, z, s16 = O.quantize_groups(np.array([[-6.5, 8.5]]))
+    assert float(s16[0, 0]) == 1.0 and int(z[0, 0]) == 6
+    assert list(q[0, 0, :2]) == [0, 14]
+    # the same groups through the container: one row per group, fp16 inputs
+    W = np.zeros((2, 3), np.float16)
+    W[0] = [0.0, 15.0, 2.5]
+    W[1] = [-6.5, 8.5, 0.0]
+    u = O.unpack(O.pack(W, np.ones(3, np.float16)))
+    assert u["n_out"] == 0
+    assert list(u["q"][0, 0, :3]) == [0, 15, 2] and int(u["z"][0, 0]) == 0
+    assert list(u["q"][1, 0, :3]) == [0, 14, 6] and int(u["z"][1, 0]) == 6
+
+
+def test_scale_ties_round_half_to_even():
+    # (hi - lo)/15 exactly halfway between two binary16 values: 1 + 2^-11 goes
+    # down to 1 (even significand), 1 + 3*2^-11 up to 1 + 2^-9 (even), where
+    # truncation would give 1 + 2^-10 and rounding half up 1 + 2^-10 for both.
+    q, z, s16 = O.quantize_groups(np.array([[0.0, 15.0 + 15 * 2.0 ** -11], [0.0, 15.0 + 45 * 2.0 ** -11]]))
+    assert float(s16[0, 0]) == 1.0
+    assert float(s16[1, 0]) == 1.0 + 2.0 ** -9
+    # through the container with fp16 inputs: lo = -15*2^-11 and -45*2^-11
+    W = np.zeros((4, 32), np.float16)
+    W[0, 0], W[0, 1] = 15.0, -15 * 2.0 ** -11
+    W[1, 0], W[1, 1] = 15.0, -45 * 2.0 ** -11
+    W[2, 0], W[2, 1] = 7.5, -15 * 2.0 ** -12
+    W[3, 0], W[3, 1] = -3.0, 2.0 ** -14
+    s = O.unpack(O.pack(W, np.ones(32, np.float16)))["s16"]
+    assert float(s[0, 0]) == 1.0 and float(s[1, 0]) == 1.0 + 2.0 ** -9
+    assert float(s[2, 0]) == 0.5                     # 0.5 + 2^-12 is a tie -> 0.5
+    # (3 + 2^-14)/15 = 0.2000041 lies between 1638 * 2^-13 and 1639 * 2^-13: nearest is the lower
+    assert float(s[3, 0]) == 1638 * 2.0 ** -13
+
+
+# --------------------------------------------------------------------------
+# KV attention tolerance: a value computed by hand
+# --------------------------------------------------------------------------
+def test_kv_attend_tolerance_hand_value():
+    # Two cached tokens, one head of two channels.  q = (1, 0); keys give
+    # scores 0 and ln 3 after the 1/sqrt(2) scaling, so p = (1/4, 3/4).
+    # V = (2, -4), (-8, 1): out = p V = (-5.5, -0.25); the bound is
+    # 1e-3 * p |V| + 1e-6 = 1e-3 * (6.5, 1.75) + 1e-6.
+    q = np.array([[1.0, 0.0]], np.float16)
+    K_hat = np.array([[[0.0, 0.0]], [[np.log(3.0) * np.sqrt(2.0), 0.0]]])
+    V_hat = np.array([[[2.0, -4.0]], [[-8.0, 1.0]]])
+    out = O.kv_attend_ref(q, K_hat, V_hat)
+    np.testing.assert_allclose(out[0], [-5.5, -0.25], rtol=1e-12)
+    tol = O.kv_attend_tolerance(q, K_hat, V_hat)
+    np.testing.assert_allclose(tol[0], [6.5e-3 + 1e-6, 1.75e-3 + 1e-6], rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# the library's hand-written binary64 -> binary16 conversion against numpy
+# --------------------------------------------------------------------------
+def _conversion_lib(tmp_path_factory):
+    import ctypes
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else None)
+    if hipcc is None:
+        pytest.skip("hipcc is not available to build the host harness")
+    d = tmp_path_factory.mktemp("fp16conv")
+    so = str(d / "libconv.so")
+    src = os.path.join(os.path.dirname(__file__), "fp16_conversion_harness.hip")
+    r = subprocess.run([hipcc, "-O2", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950", src, "-o", so],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    lib = ctypes.CDLL(so)
+    lib.convert_batch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+    return lib
+
+
+def test_device_fp16_conversion_matches_numpy(tmp_path_factory):
+    """Every finite binary16 value, every midpoint between neighbours (ties),
+    points just either side of each midpoint, the subnormal range, overflow
+    and the smallest magnitudes: the library's conversion equals numpy's
+    float64 -> float16 (round to nearest, ties to even) bit for bit."""
+    lib = _conversion_lib(tmp_path_factory)
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    h = bits.view(np.float16)
+    fin = np.isfinite(h)
+    vals = h[fin].astype(np.float64)
+    pos = np.sort(np.unique(np.abs(vals)))
+    nxt = np.append(pos[1:], 65536.0)  # 2^16: the value past the largest finite one
+    mids = (pos + nxt) / 2
+    probes = np.concatenate([
+        vals, mids, -mids,
+        np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf),
+        -np.nextafter(mids, np.inf), -np.nextafter(mids, -np.inf),
+        [2.0 ** -25, -2.0 ** -25, 2.0 ** -26, 3 * 2.0 ** -26, 2.0 ** -30, 1e-300, 5e-324, 0.0, -0.0,
+         65519.99, 65520.0, 65536.0, 1e6, -1e6, 1e300, np.inf, -np.inf],
+    ])
+    got = np.empty(probes.size, np.uint16)
+    lib.convert_batch(probes.ctypes.data, got.ctypes.data, probes.size)
+    with np.errstate(over="ignore"):  # values past the binary16 range become infinities
+        want = probes.astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} differ; first {probes[bad[0]]!r}: {got[bad[0]]:#06x} vs numpy {want[bad[0]]:#06x}"
+    nan = np.array([np.nan], np.float64)
+    out = np.empty(1, np.uint16)
+    lib.convert_batch(nan.ctypes.data, out.ctypes.data, 1)
+    assert (int(out[0]) & 0x7C00) == 0x7C00 and (int(out[0]) & 0x03FF) != 0  # a NaN stays a NaN
