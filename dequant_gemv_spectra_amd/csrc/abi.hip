@@ -463,6 +463,39 @@ HandleTable<spectra_step>& steps() {
 }  // namespace
 }  // namespace spectra
 
+// ---- the no-allocation product's scratch ----
+// A fixed device array that the MFMA path of spectra_gemm_noalloc uses as its
+// workspace (x permuted to bulk order), so that call allocates nothing.  Each
+// GPU the library runs on holds its own copy for the life of the process.
+// In host code the array's name is only a host-side stand-in: its device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever handed to a kernel.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace spectra {
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch` per device, once looked up
+
+// The scratch address on `device`, which must be the current device.
+hipError_t scratch_on(int device, void** out) {
+  if (device < 0 || device >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
+}  // namespace
+}  // namespace spectra
+
 using namespace spectra;
 
 extern "C" {
@@ -612,6 +645,39 @@ int spectra_gemm_ex(const spectra_container* h, const void* x, void* y, int64_t 
     void* ws = nullptr;
     e = stream_workspace(c->device, s, mfma_workspace_bytes(v, M), &ws);
     if (e != hipSuccess) return fail(SPECTRA_E_NOMEM, hip_msg("MFMA workspace", e));
+    e = launch_mfma_ws(v, xp, yp, M, ws, s);
+  }
+  if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("kernel launch", e));
+  return SPECTRA_OK;
+}
+
+int spectra_gemm_noalloc(const spectra_container* h, const void* x, void* y, int64_t M, void* stream, int kernel) {
+  const spectra_container* c = cont(h);
+  if (!c) return fail(SPECTRA_E_INVAL, "invalid or freed container");
+  if (!x || !y) return fail(SPECTRA_E_INVAL, "null x or y");
+  if ((reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(y) & 3))
+    return fail(SPECTRA_E_INVAL, "x and y must be 4-byte aligned");
+  const int st = check_gemm_args(c, M, kernel);
+  if (st != SPECTRA_OK) return st;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("hipGetDevice", e));
+  if (cur != c->device) return fail(SPECTRA_E_INVAL, "the container's device must be the current device");
+  const DeviceView v = c->view();
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  uint16_t* yp = static_cast<uint16_t*>(y);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int plan = plan_of(v, M, kernel);
+  if (plan < 0) return plan;
+  if (plan == SPECTRA_PLAN_GEMV) {
+    e = launch_gemv(v, xp, yp, M, s);  // no workspace
+  } else {
+    const size_t need = mfma_workspace_bytes(v, M);
+    if (need > kScratchBytes)
+      return fail(SPECTRA_E_UNSUPPORTED, "the product needs " + std::to_string(need) +
+                                             " bytes of workspace, more than the 8 MiB static scratch");
+    void* ws = nullptr;
+    if ((e = scratch_on(c->device, &ws)) != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("static scratch address", e));
     e = launch_mfma_ws(v, xp, yp, M, ws, s);
   }
   if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("kernel launch", e));

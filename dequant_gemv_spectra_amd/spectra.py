@@ -25,7 +25,8 @@ SPECTRA_E_TIMEOUT = -7
 
 KERNELS = {"auto": 0, "gemv": 1, "mfma": 2}
 
-EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm_ex", "spectra_gemm_plan",
+EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm_ex", "spectra_gemm_noalloc",
+            "spectra_gemm_plan",
             "spectra_gemm_grouped", "spectra_embed", "spectra_free", "spectra_info",
             "spectra_export", "spectra_validate_image", "spectra_import", "spectra_save",
             "spectra_load", "spectra_kv_create", "spectra_kv_append", "spectra_kv_attend",
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.spectra_gemm.restype = c_int
     L.spectra_gemm_ex.argtypes = [vp, vp, vp, i64, vp, c_int]
     L.spectra_gemm_ex.restype = c_int
+    L.spectra_gemm_noalloc.argtypes = [vp, vp, vp, i64, vp, c_int]
+    L.spectra_gemm_noalloc.restype = c_int
     L.spectra_gemm_plan.argtypes = [vp, i64, c_int]
     L.spectra_gemm_plan.restype = c_int
     L.spectra_gemm_grouped.argtypes = [ctypes.POINTER(vp), c_int, vp, ctypes.POINTER(vp), i64, vp]
@@ -242,6 +245,21 @@ def spectra_gemm(c: Container, x, y=None, stream=None, kernel: str = "auto"):
         raise ValueError("y must be a contiguous float16 tensor of shape [M][N]")
     _check(lib().spectra_gemm_ex(c.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
                                  M, _stream_ptr(stream), KERNELS[kernel]))
+    return y
+
+
+def spectra_gemm_noalloc(c: Container, x, y, stream=None, kernel: str = "auto"):
+    """As spectra_gemm into a given y, through the entry point that allocates
+    no device memory (the MFMA path uses the library's static scratch)."""
+    import torch
+    info = c.info()
+    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.shape[1] != info["K"]:
+        raise ValueError("x must be a CUDA float16 tensor of shape [M][K]")
+    M = x.shape[0]
+    if y.dtype != torch.float16 or not y.is_contiguous() or tuple(y.shape) != (M, info["N"]):
+        raise ValueError("y must be a contiguous float16 tensor of shape [M][N]")
+    _check(lib().spectra_gemm_noalloc(c.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                      M, _stream_ptr(stream), KERNELS[kernel]))
     return y
 
 

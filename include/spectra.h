@@ -176,6 +176,20 @@ int spectra_gemm(const spectra_container* c, const void* x, void* y, int64_t M);
 int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t M,
                     void* stream, int kernel);
 
+/* spectra_gemm_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same product and kernels, bit for bit, but the MFMA path's workspace
+ * (x permuted to bulk order, M * (32 G + n_out rounded up to 32) * 2 bytes)
+ * is a static 8 MiB device array of the library instead of the per-stream
+ * workspace, and the call makes no device allocation at all.  The
+ * container's device must be the current device (E_INVAL otherwise); a
+ * product whose workspace exceeds 8 MiB returns SPECTRA_E_UNSUPPORTED and
+ * enqueues nothing.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams, other threads) race and must be
+ * serialized by the caller. */
+int spectra_gemm_noalloc(const spectra_container* c, const void* x, void* y, int64_t M,
+                         void* stream, int kernel);
+
 /* Which kernel spectra_gemm_ex would run for M rows of x and the selector
  * `kernel` (a spectra_kernel), without any device work: the product is the
  * fused dequantize-and-multiply of spectra_gemm (SPECTRA page, abstract and

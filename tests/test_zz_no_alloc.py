@@ -1,0 +1,46 @@
+"""The product entry point that allocates nothing (spectra_gemm_noalloc),
+through the C ABI: its outputs equal spectra_gemm_ex's bit for bit and meet
+the oracle bound, on two calls in a row (the second with a smaller input),
+and a workspace larger than its static scratch is refused."""
+import numpy as np
+import pytest
+
+from dequant_gemv_spectra_amd import synth
+from oracle import spectra_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def test_noalloc_matches_gemm_ex_on_consecutive_calls():
+    import torch
+    from dequant_gemv_spectra_amd import spectra as sp
+    W, g, _ = synth.random_case(700, 2600, 30, 123)
+    c = sp.spectra_pack(W, g)
+    W_hat = O.unpack(sp.spectra_export(c))["W_hat"]
+    rng = np.random.default_rng(123)
+    for M, kernel in ((64, "mfma"), (9, "mfma"), (5, "auto"), (1, "auto")):  # larger, then smaller inputs
+        x = rng.standard_normal((M, 2600)).astype(np.float16)
+        xd = torch.from_numpy(x).cuda()
+        y_ref = sp.spectra_gemm(c, xd, kernel=kernel)
+        y = torch.full((M, 700), 3.0, dtype=torch.float16, device="cuda")
+        sp.spectra_gemm_noalloc(c, xd, y, kernel=kernel)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"M={M} ({kernel}): differs from spectra_gemm_ex"
+        err = np.abs(y.cpu().numpy().astype(np.float64) - O.matmul_ref(W_hat, x))
+        assert (err <= O.tolerance(W_hat, x)).all(), f"M={M}: outside the oracle bound"
+    c.close()
+
+
+def test_noalloc_refuses_a_workspace_past_its_scratch():
+    import torch
+    from dequant_gemv_spectra_amd import spectra as sp
+    W, g, _ = synth.random_case(64, 8192, 0, 124)
+    c = sp.spectra_pack(W, g)
+    M = 600  # 600 * 8192 * 2 bytes > 8 MiB
+    x = torch.zeros((M, 8192), dtype=torch.float16, device="cuda")
+    y = torch.zeros((M, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(sp.SpectraError) as e:
+        sp.spectra_gemm_noalloc(c, x, y, kernel="mfma")
+    assert e.value.status == sp.SPECTRA_E_UNSUPPORTED
+    assert "8 MiB" in str(e.value)
+    c.close()
