@@ -28,6 +28,7 @@ SOURCES = {
     "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"],
     "mfma.hip": [],
     "step.hip": [],
+    "image.cpp": [],  # host-only code
     "embed.hip": [],
     # k_kv_combine's scalar arguments preloaded into scalar registers as well
     "kv.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-kernarg-preload-count=14"],
@@ -47,7 +48,7 @@ def hipcc() -> str:
 
 
 def _compile(src: str, extra: list, verbose: bool) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -94,6 +94,24 @@ namespace spectra {
 void set_error(const std::string& msg, int status);
 int fail(int status, const std::string& msg);
 
+// ---- container images on the host (image.cpp) ----
+// Shape limits of a container (status; message set on failure).
+int check_shape(int64_t K, int64_t N);
+struct ImageFields {
+  int64_t K, N, K_b, G, n_out;
+  Layout lay;
+};
+// Header checks: fields, shape limits, offsets equal to the layout, total.
+int parse_header(const unsigned char* h, uint64_t bytes, ImageFields& f);
+// Checks on the bytes [pos, pos + len) of the image (any split into ranges at
+// even positions): scales finite and >= 0, heavy-tailed weights finite, the
+// zero nibble past N*G zero.
+int check_range(const ImageFields& f, uint64_t pos, const unsigned char* p, uint64_t len);
+// mask: n_out bits set, none past K; perm: the canonical channel order.
+int check_meta(const ImageFields& f, const uint32_t* mask, const int32_t* perm);
+// All of the above on a whole host image.
+int validate_host_image(const unsigned char* img, uint64_t bytes, ImageFields& f);
+
 // ---- packer (pack.hip) ----
 // Scratch needed by the kurtosis passes for a K x N matrix, in bytes.
 uint64_t kurtosis_scratch_bytes(int64_t K, int64_t N);
