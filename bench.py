@@ -79,7 +79,8 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha(files=("gemv.hip", "mfma.hip", "spectra_internal.h")):
+def kernel_sources_sha(files=("gemv.hip", "gemv_common.h", "mfma.hip")):
+    """Hash of the product kernels' sources: stored counter figures are valid while it holds."""
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "dequant_gemv_spectra_amd", "csrc", f), "rb") as fh:
