@@ -21,11 +21,21 @@
 // row c's record, members 8r .. 8r + 7 of the group.  The dword is
 // dequantized in registers to exact fp16 (q - z): (w & 0x000F000F) | 0x6400
 // 6400 holds 1024 + q of two members, (w & 0x00F000F0) | 0x5400 5400 holds
-// 64 + q of the next two, and subtracting 1024 + z or 64 + z is exact.  One
-// MFMA per group and m-subtile into a zero accumulator, then acc += s16 * D in
-// fp32, so the weights are never rounded a second time.  The A operand (x in
-// bulk order, 16*MT rows x 32*CG positions per chunk) is staged in LDS once per
-// block and chunk; the weights run 4 chunks ahead in registers.  The
+// 64 + q of the next two, and subtracting 1024 + z or 64 + z is exact.  The
+// B operand is then fp16(s16 * (q - z)): each dequantized weight rounded once
+// to fp16, the tensor-core form of the weights, and one MFMA per group and
+// m-subtile accumulates straight into the fp32 sum, with no vector-ALU work
+// between MFMAs.  The rounding adds at most 2^-11 |w_hat| per weight (2^-25
+// absolute below fp16's normal range), inside the product's tolerance
+// 1e-3 |W_hat| |x|.  A row whose scales reach 4096 (15 s16 could pass fp16's
+// range) switches, from the first such group on, to operands scaled by
+// 2^-12: its running sum is multiplied by 2^-12 once (exact) and its outputs
+// by 2^12 at the store.  A block is 7 compute waves and one loader wave:
+// the loader streams the A operand (x in bulk order, 16*MT rows x 32*CG
+// positions per chunk) into a ring of 4 LDS buffers by LDS-DMA, three
+// chunks ahead of the compute waves, and a barrier per chunk hands each
+// buffer over; the compute waves keep their weights 4 chunks ahead in
+// registers and issue no other loads in the loop.  The
 // heavy-tailed columns follow as plain MFMA steps (fp16 weights, scale 1).
 // Loads use buffer descriptors: rows past N or M and positions past the
 // padded K read as zero.
@@ -35,9 +45,9 @@ namespace spectra {
 namespace {
 
 constexpr int kThreads = 256;   // k_xbulk
-constexpr int kMaxW = 8;        // waves per block (4 .. 8)
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOob = 0x80000000u;
+constexpr int kStreamNt = 2;   // cache-policy bit nt on code records (read once)
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -91,6 +101,20 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t z) {
   return half8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// Scales of 4096 and more: 15 s16 may pass 65504, fp16's largest finite value
+// (scales are never negative, so their bits compare as integers).
+constexpr uint32_t kBigScale = 0x6C00u;  // fp16 bits of 4096
+constexpr float kDown = 1.0f / 4096.0f;
+
+// The 8 members times the group's scale and the row's exponent factor (1 or
+// 2^-12), rounded once to fp16 (the factor makes the scale's product exact
+// when it is 1; in a row of huge scales, where it is 2^-12, the tolerance is
+// as large as the weights).
+__device__ __forceinline__ half8 scale8(half8 d, uint32_t s16, _Float16 em) {
+  const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)s16) * em;
+  return d * sh;
+}
+
 // One chunk of one wave's weights, loaded with consecutive lanes on
 // consecutive records of a row (whole cache lines): for load k, lane l takes
 // record q = 64 k + l of the 16 x CG block of the tile, i.e. row q / CG and
@@ -104,39 +128,124 @@ struct WFrag {
   uint32_t s[NT][CR], z[NT][CR];
 };
 
-// CG groups per K chunk (CR = CG / 4 records per lane and tile).
+// One LDS-DMA instruction: lane l's 16 bytes at buffer offset `off` land at
+// LDS byte lds + 16 l (buffer_load_dwordx4 ... lds).  Inline assembly, so
+// the compiler neither waits on it before LDS reads nor drains it at
+// barriers; the issuing wave counts its own instructions.  M0 is saved and
+// restored; the leading s_nop keeps SGPR operands written by a VALU
+// instruction just before at the required distance.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t off) {
+  uint32_t save;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(off), "s"(r)
+      : "memory");
+}
+
+// Waits until at most n of this wave's vector memory operations are
+// outstanding (n is a compile-time count up to 63).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Block barrier for LDS hand-offs that leaves vector memory operations in
+// flight (this wave's LDS accesses complete first).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kMfmaCW = 7;                  // compute waves of k_mfma
+constexpr int kMfmaThreads = 64 * (kMfmaCW + 1);  // plus the loader wave
+constexpr int kXRing = 4;                   // x chunk buffers: the loader runs 3 chunks ahead
+
+// LDS-DMA instructions of the loader per x chunk: 16 MT rows of 32 CG
+// positions (4 CG 16-byte segments) plus one pad slot per row.
+template <int MT, int CG>
+constexpr int mfma_nx() {
+  return (16 * MT * (4 * CG + 1) + 63) / 64;
+}
+// Every instruction writes a whole 1 KB block, so a ring buffer is NX blocks.
+template <int MT, int CG>
+constexpr size_t mfma_lds_bytes() {
+  return (size_t)kXRing * mfma_nx<MT, CG>() * 1024;
+}
+
+// CG groups per K chunk (CR = CG / 4 records per lane and tile).  Waves
+// 0 .. 6 compute (16 NT rows each), wave 7 streams x.
 template <int MT, int NT, int CG>
-__global__ __launch_bounds__(64 * kMaxW) void k_mfma(const DeviceView v, const uint16_t* __restrict__ xw,
-                                                     int KW, int64_t M, uint16_t* __restrict__ y) {
+__global__ __launch_bounds__(kMfmaThreads) void k_mfma(const DeviceView v, const uint16_t* __restrict__ xw,
+                                                       int KW, int64_t M, uint16_t* __restrict__ y) {
   constexpr int BM = 16 * MT;
   constexpr int CR = CG / 4;
   constexpr int CK = 32 * CG;       // bulk positions per chunk
   constexpr int RowH = CK + 8;      // LDS row stride in halves (16 bytes of pad: conflict-free reads)
   constexpr int SEG = CK / 8;       // 16-byte x segments per row and chunk
-  constexpr int XS = BM * SEG / 256;  // x segments per thread and chunk (at least 4 waves)
+  constexpr int SLOTS = BM * (SEG + 1);   // LDS slots of one chunk (pad slot per row)
+  constexpr int NX = mfma_nx<MT, CG>();   // loader DMA instructions per chunk
+  constexpr int XB = NX * 512;            // halves per ring buffer (whole 1 KB blocks)
+  static_assert(NX * 64 >= SLOTS, "slots");
+  constexpr int XWAIT = 2 * NX < 63 ? 2 * NX : 63;  // the loader's wait: two later chunks may stay in flight
   constexpr int TRS = 16 * CG + 16;                 // LDS row stride of a code tile, bytes
   constexpr int TB = 16 * TRS + 16 * CG * 2 + 16 * CG;  // codes, scales, zero bytes of one tile
-  __shared__ __align__(16) uint16_t As[2][BM * RowH];
-  __shared__ __align__(16) unsigned char Wt[kMaxW][NT][TB];
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem);  // [kXRing][XB]: rows of RowH halves
+  __shared__ __align__(16) unsigned char Wt[kMfmaCW][NT][TB];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int nthreads = blockDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int W = nthreads >> 6;
   const int r4 = lane >> 4, c = lane & 15;
   const int G = v.G, KP = 32 * G;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int64_t rowA = ((int64_t)blockIdx.x * W + wave) * (16 * NT);  // this wave's first row
+  const int64_t rows_m = (M - m0) < BM ? (M - m0) : BM;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(xw + m0 * KW, (uint64_t)rows_m * KW * 2);
+  const int nchunk = (G + CG - 1) / CG;
+  const int nsteps = (nchunk + 15) & ~15;  // the compute loop is unrolled by 16
+
+  if (wave == kMfmaCW) {
+    // loader: chunk ch of x (rows m0 .. m0 + BM - 1, positions ch CK ..) into
+    // ring buffer ch % 4, slot s = (row, segment) with one pad slot per row;
+    // chunks past the last one (and positions past 32G) read zeros, so every
+    // step issues the same NX instructions and the wait counts hold
+    const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(smem);
+    auto issue = [&](int ch) {
+      const uint32_t base = ring + (uint32_t)((ch & (kXRing - 1)) * XB * 2);
+#pragma unroll
+      for (int k = 0; k < NX; ++k) {
+        const int s = 64 * k + lane, row = s / (SEG + 1), sg = s % (SEG + 1);
+        const int col = ch * CK + 8 * sg;
+        const bool ok = s < SLOTS && sg < SEG && col < KP;
+        dma16(rx, base + 1024u * (uint32_t)k, ok ? (uint32_t)(row * KW + col) * 2u : kOob);
+      }
+    };
+    issue(0);
+    issue(1);
+    issue(2);
+    for (int ch = 0; ch < nsteps; ++ch) {
+      vm_wait<XWAIT>();  // chunk ch has landed
+      lds_barrier();     // step ch: chunk ch is visible; buffer (ch + 3) % 4 is free
+      issue(ch + 3);
+    }
+    return;
+  }
+
+  const int64_t rowA = ((int64_t)blockIdx.x * kMfmaCW + wave) * (16 * NT);  // this wave's first row
   const int64_t left = v.N - rowA;
   const int rows = left <= 0 ? 0 : (left < 16 * NT ? (int)left : 16 * NT);
-  const int64_t rows_m = (M - m0) < BM ? (M - m0) : BM;
-
-  // descriptors on this wave's rows and this block's x rows
+  // descriptors on this wave's rows
   const int64_t i0 = (rows > 0 ? rowA : 0) * G;
   const __amdgpu_buffer_rsrc_t rc = rsrc(v.codes + i0, (uint64_t)rows * G * 16);
   const __amdgpu_buffer_rsrc_t rs = rsrc(v.scales + i0, (uint64_t)rows * G * 2);
   const int64_t zb0 = i0 >> 1;
   const __amdgpu_buffer_rsrc_t rz = rsrc(v.zeros + zb0, (uint64_t)(((i0 + (int64_t)rows * G + 1) >> 1) - zb0));
-  const __amdgpu_buffer_rsrc_t rx = rsrc(xw + m0 * KW, (uint64_t)rows_m * KW * 2);
 
   auto load_w = [&](WFrag<NT, CR>& f, int ch) {
 #pragma unroll
@@ -146,36 +255,22 @@ __global__ __launch_bounds__(64 * kMaxW) void k_mfma(const DeviceView v, const u
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const uint32_t local = (uint32_t)((16 * t + row) * G + g);
-        f.c[t][k] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? local * 16u : kOob, 0, 0);
+        f.c[t][k] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? local * 16u : kOob, 0, kStreamNt);
         f.s[t][k] = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? local * 2u : kOob, 0, 0);
         const uint32_t zoff = (uint32_t)(((i0 + local) >> 1) - zb0);
         f.z[t][k] = __builtin_amdgcn_raw_buffer_load_b8(rz, ok ? zoff : kOob, 0, 0);
       }
     }
   };
-  // x chunk: BM rows x SEG segments of 8 halves
-  auto load_x = [&](u32x4* xr, int ch) {
-#pragma unroll
-    for (int i = 0; i < XS; ++i) {
-      const int seg = tid + nthreads * i;
-      const int mrow = seg / SEG, col = ch * CK + 8 * (seg % SEG);
-      xr[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rx, (seg < BM * SEG && col < KP) ? (uint32_t)(mrow * KW + col) * 2u : kOob, 0, 0);
-    }
-  };
-  auto store_x = [&](const u32x4* xr, uint16_t* buf) {
-#pragma unroll
-    for (int i = 0; i < XS; ++i) {
-      const int seg = tid + nthreads * i;
-      if (seg < BM * SEG) *reinterpret_cast<u32x4*>(buf + (seg / SEG) * RowH + 8 * (seg % SEG)) = xr[i];
-    }
-  };
 
   float4_t acc[NT][MT];
+  _Float16 em[NT];  // this lane's row of tile t: operand factor (1, or 2^-12 once a scale reached 4096)
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NT; ++t) {
+    em[t] = (_Float16)1.0f;
 #pragma unroll
     for (int tm = 0; tm < MT; ++tm) acc[t][tm] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto compute = [&](const WFrag<NT, CR>& f, int ch, const uint16_t* buf) {
     // this wave's records to its LDS tiles, then back in MFMA order: lane
@@ -199,70 +294,73 @@ __global__ __launch_bounds__(64 * kMaxW) void k_mfma(const DeviceView v, const u
                    ((uint32_t)tile[16 * TRS + 32 * CG + c * CG + j] << 16);
       }
     }
-    half8 a[CG][MT];
+    // a row meeting its first huge scale: sum so far times 2^-12, operands from now on too
+    bool hit[NT];
+    bool any = false;
 #pragma unroll
-    for (int j = 0; j < CG; ++j)
+    for (int t = 0; t < NT; ++t) {
+      hit[t] = false;
 #pragma unroll
-      for (int tm = 0; tm < MT; ++tm)
-        a[j][tm] = *reinterpret_cast<const half8*>(buf + (16 * tm + c) * RowH + 32 * j + 8 * r4);
+      for (int j = 0; j < CG; ++j) hit[t] |= (sz[t][j] & 0xFFFFu) >= kBigScale;
+      hit[t] = hit[t] && em[t] == (_Float16)1.0f;
+      any |= hit[t];
+    }
+    if (__builtin_expect(__ballot(any) != 0, 0)) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (hit[t]) {
+          em[t] = (_Float16)kDown;
+#pragma unroll
+          for (int tm = 0; tm < MT; ++tm) acc[t][tm] *= kDown;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
       const int g = ch * CG + j;
       if (g >= G) break;  // uniform: the last chunk may be partial
+      half8 a[MT];  // x of group j for each m-subtile
+#pragma unroll
+      for (int tm = 0; tm < MT; ++tm)
+        a[tm] = *reinterpret_cast<const half8*>(buf + (16 * tm + c) * RowH + 32 * j + 8 * r4);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const uint32_t par = (uint32_t)((i0 + (int64_t)(16 * t + c) * G + g) & 1);
         const uint32_t z = (sz[t][j] >> (16u + 4u * par)) & 0xFu;
-        const half8 b = dequant_word(R[t][j], z);
-        const float sc = h2f((uint16_t)sz[t][j]);
+        const half8 b = scale8(dequant_word(R[t][j], z), sz[t][j] & 0xFFFFu, em[t]);
 #pragma unroll
-        for (int tm = 0; tm < MT; ++tm) {
-          const float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j][tm], b, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          acc[t][tm] += sc * p;
-        }
+        for (int tm = 0; tm < MT; ++tm)
+          acc[t][tm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tm], b, acc[t][tm], 0, 0, 0);
       }
     }
   };
 
-  // x chunks run kXD steps ahead in registers (kXD register sets), then go
-  // to one of two LDS buffers the step before they are used; weights run
-  // 4 chunks ahead (f0 .. f3).  The loop is unrolled by 4 so every register
-  // set is addressed at compile time.
-  constexpr int kXD = XS >= 4 ? 2 : 4;
-  const int nchunk = (G + CG - 1) / CG;
-  u32x4 xr[kXD][XS];
+  // Weights run 4 chunks ahead in registers (f0 .. f3); x chunk ch is in
+  // ring buffer ch % 4 from step ch's barrier on.  The loop is unrolled by
+  // 16 so every register set is addressed at compile time and the compiler
+  // keeps exact wait counts for the weights inside an iteration (at the loop
+  // header it waits for every load in flight: once per 16 chunks); steps
+  // past the last chunk multiply nothing, and no step exits early.
   WFrag<NT, CR> f0, f1, f2, f3;
-  // prologue in the steady state's issue order (weights, then x, per chunk)
   load_w(f0, 0);
-  load_x(xr[0], 0);
   load_w(f1, 1);
-  load_x(xr[1 % kXD], 1);
   load_w(f2, 2);
-  if constexpr (kXD > 2) load_x(xr[2 % kXD], 2);
   load_w(f3, 3);
-  if constexpr (kXD > 3) load_x(xr[3 % kXD], 3);
-  store_x(xr[0], As[0]);
-  __syncthreads();
-  // One step: multiply chunk ch, refill its weight buffer with chunk ch + 4,
-  // publish chunk ch + 1's x and request chunk ch + kXD's.
-  auto step = [&](WFrag<NT, CR>& f, int ch, u32x4* x_next, u32x4* x_free) {
-    compute(f, ch, As[ch & 1]);
+  auto step = [&](WFrag<NT, CR>& f, int ch) {
+    lds_barrier();
+    compute(f, ch, As + (ch & (kXRing - 1)) * XB);
     load_w(f, ch + 4);
-    store_x(x_next, As[(ch + 1) & 1]);
-    load_x(x_free, ch + kXD);
-    __syncthreads();
   };
-  // The step count is rounded up to a multiple of 4 (steps past the last
-  // chunk multiply nothing) so the unrolled body has no early exits: the
-  // compiler then keeps exact wait counts across the loop.
-  for (int ch = 0; ch < nchunk; ch += 4) {
-    step(f0, ch, xr[1 % kXD], xr[0]);
-    step(f1, ch + 1, xr[2 % kXD], xr[1 % kXD]);
-    step(f2, ch + 2, xr[3 % kXD], xr[2 % kXD]);
-    step(f3, ch + 3, xr[0], xr[3 % kXD]);
+  for (int ch = 0; ch < nsteps; ch += 16) {
+#pragma unroll
+    for (int u = 0; u < 16; u += 4) {
+      step(f0, ch + u);
+      step(f1, ch + u + 1);
+      step(f2, ch + u + 2);
+      step(f3, ch + u + 3);
+    }
   }
 
-  // heavy-tailed columns: fp16 weights as they are, scale 1
+  // heavy-tailed columns: fp16 weights as they are (times the row's factor)
   const int n_out = v.n_out;
   if (n_out > 0 && rows > 0) {
     const __amdgpu_buffer_rsrc_t ro = rsrc(v.outliers + rowA * n_out, (uint64_t)rows * n_out * 2);
@@ -284,7 +382,7 @@ __global__ __launch_bounds__(64 * kMaxW) void k_mfma(const DeviceView v, const u
               ro, j < n_out ? (uint32_t)((16 * t + c) * n_out + j) * 2u : kOob, 0, 0);
         }
         const half8 b = __builtin_bit_cast(
-            half8, u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
+            half8, u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)}) * em[t];
 #pragma unroll
         for (int tm = 0; tm < MT; ++tm) acc[t][tm] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tm], b, acc[t][tm], 0, 0, 0);
       }
@@ -301,7 +399,7 @@ __global__ __launch_bounds__(64 * kMaxW) void k_mfma(const DeviceView v, const u
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + 16 * tm + 4 * r4 + i;
-        if (m < M) y[m * v.N + n] = f2h(acc[t][tm][i]);
+        if (m < M) y[m * v.N + n] = f2h(em[t] == (_Float16)1.0f ? acc[t][tm][i] : acc[t][tm][i] * 4096.0f);
       }
     }
   }
@@ -329,7 +427,10 @@ __global__ __launch_bounds__(64 * kMaxW) void k_mfma(const DeviceView v, const u
 // instruction, where one scale per record lane would touch 16 rows) and pass
 // through a small wave-private LDS area, from which lane (r, c) reads the four
 // scales and zero bytes of row c and the quad.  Each group's product goes into
-// a zero accumulator and is added with its fp32 scale, as in k_mfma.  The A
+// a zero accumulator and is added with its fp32 scale: at these M the
+// products are short and the scale FMAs overlap the next group's MFMA
+// (fp16(s16 (q - z)) operands accumulated by the MFMAs, as k_mfma does,
+// measured 51.5 -> 56.1 us at 28672 x 8192, M = 8).  The A
 // operand is x in bulk order, read from LDS; lanes of rows m >= M read row
 // M - 1, and those output rows are never stored.
 // Each wave then holds a partial 16 x 16 product; the waves add theirs through
@@ -340,7 +441,6 @@ constexpr int kKsWaves = 8;
 constexpr int kKsThreads = 64 * kKsWaves;
 constexpr int kKsXSeg = 24;    // 16-byte x segments per thread staged in one round trip
 constexpr int kKsMaxQ = 10;    // quads per wave (G <= 320); more would spill registers
-constexpr int kStreamNt = 2;   // cache-policy bit nt on code records (read once)
 
 template <int Q, int OB>
 struct KsFrag {
@@ -583,31 +683,36 @@ size_t mfma_workspace_bytes(const DeviceView& v, int64_t M) {
 namespace {
 
 template <int MT, int NT>
-void launch_k(const DeviceView& v, const uint16_t* xw, int KW, int64_t M, uint16_t* y, int W,
-              hipStream_t s) {
+hipError_t launch_k(const DeviceView& v, const uint16_t* xw, int KW, int64_t M, uint16_t* y, hipStream_t s) {
   constexpr int CG = (NT == 1 && MT <= 2) ? 8 : 4;  // one tile per wave: wider chunks keep more bytes in flight
+  constexpr size_t lds = mfma_lds_bytes<MT, CG>();
+  const void* fn = reinterpret_cast<const void*>(&k_mfma<MT, NT, CG>);
+  if (lds > 64 * 1024) {  // dynamic LDS past 64 KiB must be allowed per kernel
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   const int64_t tiles = (v.N + 15) / 16;
-  const int64_t bx = (tiles + (int64_t)W * NT - 1) / ((int64_t)W * NT);
+  const int64_t bx = (tiles + (int64_t)kMfmaCW * NT - 1) / ((int64_t)kMfmaCW * NT);
   const int64_t by = (M + 16 * MT - 1) / (16 * MT);
-  hipLaunchKernelGGL((k_mfma<MT, NT, CG>), dim3((unsigned)bx, (unsigned)by), dim3(64 * W), 0, s, v, xw, KW, M, y);
+  hipLaunchKernelGGL((k_mfma<MT, NT, CG>), dim3((unsigned)bx, (unsigned)by), dim3(kMfmaThreads), lds, s, v, xw,
+                     KW, M, y);
+  return hipGetLastError();
 }
 
-// Waves per block W (4 .. 8) and 16-row tiles per wave NT so that one block
-// row of the grid covers N with about one block per compute unit.
+// 16-row tiles per wave NT so that one block row of the grid covers N with
+// about one block per compute unit.
 template <int MT>
-void launch_mt(const DeviceView& v, const uint16_t* xw, int KW, int64_t M, uint16_t* y, hipStream_t s) {
+hipError_t launch_mt(const DeviceView& v, const uint16_t* xw, int KW, int64_t M, uint16_t* y, hipStream_t s) {
   constexpr int kNTMax = MT >= 8 ? 1 : (MT >= 4 ? 2 : 4);  // accumulators: NT * MT * 4 registers
   const int64_t tiles = (v.N + 15) / 16;
   const int64_t cu = v.cu_count > 0 ? v.cu_count : 1;
   const int64_t tpc = (tiles + cu - 1) / cu;
-  auto clampw = [](int64_t w) { return (int)(w < 4 ? 4 : (w > kMaxW ? kMaxW : w)); };
-  if (tpc <= kMaxW || kNTMax == 1) {
-    launch_k<MT, 1>(v, xw, KW, M, y, clampw(tpc), s);
-  } else if (tpc <= 2 * kMaxW || kNTMax == 2) {
-    if constexpr (kNTMax >= 2) launch_k<MT, 2>(v, xw, KW, M, y, clampw((tpc + 1) / 2), s);
-  } else {
-    if constexpr (kNTMax >= 4) launch_k<MT, 4>(v, xw, KW, M, y, clampw((tpc + 3) / 4), s);
+  if (tpc <= kMfmaCW || kNTMax == 1) return launch_k<MT, 1>(v, xw, KW, M, y, s);
+  if (tpc <= 2 * kMfmaCW || kNTMax == 2) {
+    if constexpr (kNTMax >= 2) return launch_k<MT, 2>(v, xw, KW, M, y, s);
   }
+  if constexpr (kNTMax >= 4) return launch_k<MT, 4>(v, xw, KW, M, y, s);
+  return hipErrorNotSupported;
 }
 
 struct KsShape {
@@ -693,11 +798,10 @@ hipError_t launch_mfma_ws(const DeviceView& v, const uint16_t* x, uint16_t* y, i
   hipLaunchKernelGGL(k_xbulk, dim3((unsigned)((KW + kThreads - 1) / kThreads), gy),
                      dim3(kThreads), 0, s, v, x, M, xw, KW);
   if (ks_supports(v, KW, M)) return launch_ks(v, xw, KW, M, y, s);
-  if (M <= 16) launch_mt<1>(v, xw, KW, M, y, s);
-  else if (M <= 32) launch_mt<2>(v, xw, KW, M, y, s);
-  else if (M <= 64) launch_mt<4>(v, xw, KW, M, y, s);
-  else launch_mt<8>(v, xw, KW, M, y, s);
-  return hipGetLastError();
+  if (M <= 16) return launch_mt<1>(v, xw, KW, M, y, s);
+  if (M <= 32) return launch_mt<2>(v, xw, KW, M, y, s);
+  if (M <= 64) return launch_mt<4>(v, xw, KW, M, y, s);
+  return launch_mt<8>(v, xw, KW, M, y, s);
 }
 
 }  // namespace spectra

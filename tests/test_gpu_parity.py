@@ -513,6 +513,25 @@ def test_mfma_product_small(N, K, n_out, seed, M):
     check_product(c, img, x, kernel="mfma")
 
 
+@pytest.mark.parametrize("M", [6, 24, 40, 128])
+def test_mfma_rows_of_huge_scales(M):
+    """Groups whose scale reaches 4096 (15 s16 would pass fp16's range as an
+    fp16 operand): their rows switch to operands scaled by 2^-12, and every
+    output, the ordinary rows of the same 16-row tiles included, stays within
+    the oracle's bound.  Columns 64 .. 95 hold U(-60000, 60000) in rows 0 .. 71
+    (kurtosis 2.4 over the column: bulk channels, one group of scale ~8000 per
+    row) and ordinary values in rows 72 .. 95."""
+    W, g, x = synth.random_case(96, 1024, 4, 60, M=M)
+    rng = np.random.default_rng(61)
+    W[:72, 64:96] = rng.uniform(-60000, 60000, (72, 32)).astype(np.float16)
+    x = (x.astype(np.float32) * 1e-3).astype(np.float16)  # keeps y inside fp16's range
+    c, img = check_pack(W, g)
+    u = O.unpack(img)
+    s = u["s16"].astype(np.float32)
+    assert (s[:72].max(axis=1) >= 4096).all() and (s[72:] < 4096).all()
+    check_product(c, img, x, kernel="mfma")
+
+
 def test_mfma_at_m1_and_gemv_agree_with_oracle():
     W, g, x = synth.random_case(700, 2560, 30, 41, M=1)
     c, img = check_pack(W, g)
