@@ -79,8 +79,13 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha(files=("gemv.hip", "gemv_common.h", "mfma.hip")):
-    """Hash of the product kernels' sources: stored counter figures are valid while it holds."""
+GEMV_SOURCES = ("gemv.hip", "gemv_common.h")
+MFMA_SOURCES = ("mfma.hip",)
+STEP_SOURCES = ("step.hip", "gemv_common.h")
+
+
+def kernel_sources_sha(files=GEMV_SOURCES):
+    """Hash of a kernel's sources: stored counter figures are valid while it holds."""
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "dequant_gemv_spectra_amd", "csrc", f), "rb") as fh:
@@ -384,7 +389,7 @@ def run_step(args, sp, torch, name, units):
         with open(TRAFFIC_FILE) as fh:
             tr = json.load(fh)
         ent = tr.get("entries", {}).get(f"{args.workload}:M1:step")
-        if ent and ent.get("source_sha") == kernel_sources_sha(("step.hip", "gemv_common.h", "spectra_internal.h")):
+        if ent and ent.get("source_sha") == kernel_sources_sha(STEP_SOURCES):
             roofline["traffic"] = int(ent["hbm_bytes_per_launch"])
     except (OSError, ValueError):
         pass
@@ -605,7 +610,8 @@ def main():
             tr = json.load(fh)
         key = f"{args.workload}:M{args.M}:{dom}"
         ent = tr.get("entries", {}).get(key)
-        if ent and ent.get("source_sha") == kernel_sources_sha():
+        srcs = GEMV_SOURCES if kernel_name == "k_gemv_m1" else MFMA_SOURCES
+        if ent and ent.get("source_sha") == kernel_sources_sha(srcs):
             roofline["traffic"] = int(ent["hbm_bytes_per_launch"])
     except (OSError, ValueError):
         pass
