@@ -82,6 +82,41 @@ WorkspaceCache& workspace_cache() {
 }
 }  // namespace
 
+// ---- device and pinned-host allocation, with a test hook ----
+// spectra_test_fail_allocations(skip, count): the next `skip` allocations
+// succeed, the `count` after them fail as out of memory.
+namespace {
+std::mutex g_alloc_mu;
+int64_t g_alloc_skip = 0, g_alloc_fail = 0;
+
+bool injected_failure() {
+  std::lock_guard<std::mutex> lk(g_alloc_mu);
+  if (g_alloc_fail <= 0) return false;
+  if (g_alloc_skip > 0) {
+    --g_alloc_skip;
+    return false;
+  }
+  --g_alloc_fail;
+  return true;
+}
+}  // namespace
+
+hipError_t dev_malloc(void** p, size_t bytes) {
+  if (injected_failure()) {
+    *p = nullptr;
+    return hipErrorOutOfMemory;
+  }
+  return hipMalloc(p, bytes);
+}
+
+hipError_t pinned_malloc(void** p, size_t bytes) {
+  if (injected_failure()) {
+    *p = nullptr;
+    return hipErrorOutOfMemory;
+  }
+  return hipHostMalloc(p, bytes, hipHostMallocDefault);
+}
+
 hipError_t stream_workspace(int device, hipStream_t s, size_t bytes, void** out) {
   WorkspaceCache& wc = workspace_cache();
   std::lock_guard<std::mutex> lk(wc.mu);
@@ -93,7 +128,7 @@ hipError_t stream_workspace(int device, hipStream_t s, size_t bytes, void** out)
   size_t nb = bytes < 2 * e.second ? 2 * e.second : bytes;
   if (nb < (1u << 20)) nb = 1u << 20;
   void* p = nullptr;
-  const hipError_t err = hipMalloc(&p, nb);
+  const hipError_t err = dev_malloc(&p, nb);
   if (err != hipSuccess) return err;
   if (e.first) wc.retired.emplace_back(device, e.first);  // work or graphs on s may still use it
   e = std::make_pair(p, nb);
@@ -182,12 +217,12 @@ spectra_container* pack_impl(const uint16_t* W_dev, const uint16_t* g_dev, int64
   }
   const uint64_t mask_words = (uint64_t)((K + 31) / 32);
   DevBuf scratch, status;
-  e = hipMalloc(&scratch.p, kurtosis_scratch_bytes(K, N));
+  e = dev_malloc(&scratch.p, kurtosis_scratch_bytes(K, N));
   if (e != hipSuccess) {
     set_error(hip_msg("hipMalloc (kurtosis scratch)", e), SPECTRA_E_NOMEM);
     return nullptr;
   }
-  e = hipMalloc(&status.p, 4 * (1 + mask_words));
+  e = dev_malloc(&status.p, 4 * (1 + mask_words));
   if (e != hipSuccess) {
     set_error(hip_msg("hipMalloc (status)", e), SPECTRA_E_NOMEM);
     return nullptr;
@@ -226,7 +261,7 @@ spectra_container* pack_impl(const uint16_t* W_dev, const uint16_t* g_dev, int64
   c->G = (c->K_b + kGroup - 1) / kGroup;
   c->lay = make_layout(K, N, n_out);
   DevBuf img;
-  e = hipMalloc(&img.p, c->lay.total);
+  e = dev_malloc(&img.p, c->lay.total);
   if (e != hipSuccess) {
     delete c;
     set_error(hip_msg("hipMalloc (container)", e), SPECTRA_E_NOMEM);
@@ -286,7 +321,7 @@ spectra_container* new_container(const ImageFields& f) {
   c->n_out = f.n_out;
   c->lay = f.lay;
   void* p = nullptr;
-  e = hipMalloc(&p, f.lay.total);
+  e = dev_malloc(&p, f.lay.total);
   if (e != hipSuccess) {
     delete c;
     set_error(hip_msg("hipMalloc (container)", e), SPECTRA_E_NOMEM);
@@ -396,6 +431,17 @@ const char* spectra_last_error(void) { return g_last_error.c_str(); }
 
 int spectra_last_status(void) { return g_last_status; }
 
+int spectra_test_fail_allocations(int64_t skip, int64_t count) {
+  if (skip < 0 || count < 0) return fail(SPECTRA_E_INVAL, "skip and count must be >= 0");
+  {
+    std::lock_guard<std::mutex> lk(g_alloc_mu);
+    g_alloc_skip = skip;
+    g_alloc_fail = count;
+  }
+  set_error("", SPECTRA_OK);
+  return SPECTRA_OK;
+}
+
 int spectra_release_workspaces(void) {
   const int st = release_workspaces();
   if (st != SPECTRA_OK) return fail(st, "freeing a retired workspace failed");
@@ -424,7 +470,7 @@ spectra_container* spectra_pack(const uint16_t* W, const uint16_t* gamma, int64_
   DevBuf wd, gd;
   hipError_t e;
   const size_t wbytes = 2ull * (uint64_t)N * (uint64_t)K;
-  if ((e = hipMalloc(&wd.p, wbytes)) != hipSuccess || (e = hipMalloc(&gd.p, 2ull * K)) != hipSuccess) {
+  if ((e = dev_malloc(&wd.p, wbytes)) != hipSuccess || (e = dev_malloc(&gd.p, 2ull * K)) != hipSuccess) {
     set_error(hip_msg("hipMalloc (staging W/gamma)", e), SPECTRA_E_NOMEM);
     return nullptr;
   }
@@ -651,7 +697,7 @@ int spectra_save(const spectra_container* h, const char* path, uint64_t chunk_by
   if (!path) return fail(SPECTRA_E_INVAL, "null path");
   const uint64_t chunk = chunk_size(chunk_bytes);
   Pinned stage;
-  hipError_t e = hipHostMalloc(&stage.p, chunk, hipHostMallocDefault);
+  hipError_t e = pinned_malloc(&stage.p, chunk);
   if (e != hipSuccess) return fail(SPECTRA_E_NOMEM, hip_msg("pinned staging buffer", e));
   int st = SPECTRA_OK;
   {
@@ -700,26 +746,31 @@ spectra_container* spectra_load(const char* path, uint64_t chunk_bytes) {
     set_error(std::string("cannot rewind ") + path, SPECTRA_E_IO);
     return nullptr;
   }
+  // the container first, then the host staging and the stream: a failure
+  // leaves nothing behind
+  spectra_container* c = new_container(f);
+  if (!c) return nullptr;
   const uint64_t chunk = chunk_size(chunk_bytes);
   Pinned stage[2];
   for (int i = 0; i < 2; ++i) {
-    const hipError_t e = hipHostMalloc(&stage[i].p, chunk, hipHostMallocDefault);
+    const hipError_t e = pinned_malloc(&stage[i].p, chunk);
     if (e != hipSuccess) {
+      drop_container(c);
       set_error(hip_msg("pinned staging buffer", e), SPECTRA_E_NOMEM);
       return nullptr;
     }
   }
   hipStream_t s = nullptr;
   if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+    drop_container(c);
     set_error("stream creation failed", SPECTRA_E_HIP);
     return nullptr;
   }
   hipEvent_t done[2] = {nullptr, nullptr};
   for (int i = 0; i < 2; ++i) (void)hipEventCreateWithFlags(&done[i], hipEventDisableTiming);
-  spectra_container* c = new_container(f);
   // mask and perm are kept on the host as they pass, for the final check
   std::vector<unsigned char> meta(f.lay.codes - f.lay.mask);
-  int st = c ? SPECTRA_OK : SPECTRA_E_NOMEM;
+  int st = SPECTRA_OK;
   bool used[2] = {false, false};
   for (uint64_t pos = 0, k = 0; st == SPECTRA_OK && pos < bytes; pos += chunk, ++k) {
     const int b = (int)(k & 1);
@@ -783,7 +834,7 @@ spectra_kv* spectra_kv_create(int64_t capacity, int32_t heads, int32_t head_dim)
     return nullptr;
   }
   void* p = nullptr;
-  e = hipMalloc(&p, 2 * (rec + sc + zb));
+  e = dev_malloc(&p, 2 * (rec + sc + zb));
   if (e != hipSuccess) {
     delete kv;
     set_error(hip_msg("hipMalloc (KV cache)", e), SPECTRA_E_NOMEM);

@@ -222,6 +222,11 @@ void step_plan_free(StepPlan* p);
 // row (false: no variant runs G).
 bool gemv_variant(int G, int* L, int* P);
 
+// ---- allocation (abi.hip): every device and pinned-host allocation of the
+// library goes through these, so a test hook can make them fail ----
+hipError_t dev_malloc(void** p, size_t bytes);
+hipError_t pinned_malloc(void** p, size_t bytes);
+
 // ---- per-stream workspace (abi.hip) ----
 // A device buffer of at least `bytes` reserved for work enqueued on stream s
 // of `device`; grown on demand (growth waits for s and reallocates).

@@ -656,7 +656,7 @@ int step_plan_create(const StepPhaseSpec* ph, int nph, int device, StepPlan** ou
   pl->tag_bytes = up(4 * tag_words, 256);
   pl->dev_bytes = ctl_bytes + table_bytes + pl->tag_bytes;
   void* mem = nullptr;
-  if ((e = hipMalloc(&mem, pl->dev_bytes)) != hipSuccess) {
+  if ((e = dev_malloc(&mem, pl->dev_bytes)) != hipSuccess) {
     delete pl;
     return fail(SPECTRA_E_NOMEM, std::string("hipMalloc (step plan): ") + hipGetErrorString(e));
   }

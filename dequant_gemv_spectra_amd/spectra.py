@@ -32,7 +32,7 @@ EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm
             "spectra_load", "spectra_kv_create", "spectra_kv_append", "spectra_kv_attend",
             "spectra_kv_length", "spectra_kv_reset", "spectra_kv_export", "spectra_kv_free",
             "spectra_step_create", "spectra_step_run", "spectra_step_status", "spectra_step_test_hooks",
-            "spectra_step_free", "spectra_release_workspaces", "spectra_last_error", "spectra_last_status",
+            "spectra_step_free", "spectra_release_workspaces", "spectra_test_fail_allocations", "spectra_last_error", "spectra_last_status",
             "spectra_version"]
 
 
@@ -131,6 +131,8 @@ def lib() -> ctypes.CDLL:
     L.spectra_last_error.restype = ctypes.c_char_p
     L.spectra_release_workspaces.argtypes = []
     L.spectra_release_workspaces.restype = c_int
+    L.spectra_test_fail_allocations.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    L.spectra_test_fail_allocations.restype = c_int
     L.spectra_last_status.argtypes = []
     L.spectra_last_status.restype = c_int
     L.spectra_version.argtypes = []
@@ -472,6 +474,12 @@ def spectra_release_workspaces() -> None:
     """Free the workspaces earlier growth retired (no graph captured before a
     growth may be replayed afterwards)."""
     _check(lib().spectra_release_workspaces())
+
+
+def spectra_test_fail_allocations(skip: int, count: int) -> None:
+    """Testing hook: of the library's next device / pinned-host allocations,
+    `skip` succeed and `count` fail as out of memory; (0, 0) turns it off."""
+    _check(lib().spectra_test_fail_allocations(skip, count))
 
 
 def spectra_version() -> int:

@@ -295,6 +295,17 @@ int spectra_step_test_hooks(spectra_step* st, uint32_t poll_limit, uint32_t tag_
 void spectra_step_free(spectra_step* st);
 
 /* ---------------------------------------------------------------------------
+ * Testing the error paths: of the device and pinned-host allocations the
+ * library makes from now on (containers, staging, workspaces, KV caches,
+ * step plans, file staging), the next `skip` succeed and the `count` after
+ * them fail as out of memory, so the calling entry point returns
+ * SPECTRA_E_NOMEM (NULL for handle returns) and releases what it had
+ * allocated.  For callers' tests of their error handling; (0, 0) turns it
+ * off.  Process-wide, thread-safe.  E_INVAL for negative arguments.
+ * ------------------------------------------------------------------------- */
+int spectra_test_fail_allocations(int64_t skip, int64_t count);
+
+/* ---------------------------------------------------------------------------
  * Group-32 4-bit KV cache (SPECTRA page, abstract: the key-value cache is kept
  * in microscaled Group-32 4-bit form).  One cache holds the keys and values of
  * one attention layer for up to `capacity` tokens, `heads` cache heads of
