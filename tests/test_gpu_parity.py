@@ -532,6 +532,32 @@ def test_mfma_rows_of_huge_scales(M):
     check_product(c, img, x, kernel="mfma")
 
 
+WIDE_MFMA = [  # (N, K, planted heavy-tailed channels, seed, M): more 16-row tiles than 7 per compute unit
+    (29000, 6000, 60, 80, 16),   # k_mfma<1, 2, 4>: 16 rows of x at K = 6000 do not fit the tiled kernel's LDS
+    (60000, 6000, 60, 81, 12),   # k_mfma<1, 4, 4>
+    (29000, 256, 3, 82, 24),     # k_mfma<2, 2, 4>
+    (60000, 256, 3, 83, 24),     # k_mfma<2, 4, 4>
+    (29000, 256, 3, 84, 48),     # k_mfma<4, 2, 4>
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("N,K,n_out,seed,M", WIDE_MFMA)
+def test_mfma_wide_grids(N, K, n_out, seed, M):
+    """The per-wave MFMA kernel with 2 and 4 row tiles per wave: sampled rows
+    (the first two blocks' rows, the last 300, 2000 at random) against the
+    oracle's reconstruction of the packed image."""
+    sp = _sp()
+    W, g, x = synth.random_case(N, K, n_out, seed, M=M)
+    c = sp.spectra_pack(W, g)
+    del W
+    assert sp.spectra_gemm_plan(c, M, kernel="mfma") == "k_mfma"
+    img = sp.spectra_export(c)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([np.arange(2 * 7 * 64), rng.integers(0, N, 2000), np.arange(N - 300, N)]))
+    check_product(c, img, x, kernel="mfma", rows=rows)
+
+
 def test_mfma_at_m1_and_gemv_agree_with_oracle():
     W, g, x = synth.random_case(700, 2560, 30, 41, M=1)
     c, img = check_pack(W, g)
