@@ -93,22 +93,24 @@ __device__ __forceinline__ void read_x(const uint16_t* src16, half2_t* xr) {
 }
 
 // sum_e (q_e - z) * x_e over one record with the dequantization fused into the
-// dot products (four accumulators keep the dot2 chains short).
+// dot products: one chain of 16 v_dot2 per record (the lane's other records
+// interleave with it; four chains cost four zeroing moves and three adds per
+// record, 1 - 4 % slower on every M = 1 shape measured).
 __device__ __forceinline__ float group_dot(const uint4 c, const uint32_t z, const half2_t* xr,
                                            const Nib nb) {
   const half2_t zl = as_h2((0x6400u + z) * 0x00010001u);
   const half2_t zh = as_h2((0x5400u + (z << 4)) * 0x00010001u);
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+  float a = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t w8 = w[d] >> 8;
-    a0 = __builtin_amdgcn_fdot2(as_h2((w[d] & nb.lo) | nb.mlo) - zl, xr[4 * d + 0], a0, false);
-    b0 = __builtin_amdgcn_fdot2(as_h2((w[d] & nb.hi) | nb.mhi) - zh, xr[4 * d + 1], b0, false);
-    a1 = __builtin_amdgcn_fdot2(as_h2((w8 & nb.lo) | nb.mlo) - zl, xr[4 * d + 2], a1, false);
-    b1 = __builtin_amdgcn_fdot2(as_h2((w8 & nb.hi) | nb.mhi) - zh, xr[4 * d + 3], b1, false);
+    a = __builtin_amdgcn_fdot2(as_h2((w[d] & nb.lo) | nb.mlo) - zl, xr[4 * d + 0], a, false);
+    a = __builtin_amdgcn_fdot2(as_h2((w[d] & nb.hi) | nb.mhi) - zh, xr[4 * d + 1], a, false);
+    a = __builtin_amdgcn_fdot2(as_h2((w8 & nb.lo) | nb.mlo) - zl, xr[4 * d + 2], a, false);
+    a = __builtin_amdgcn_fdot2(as_h2((w8 & nb.hi) | nb.mhi) - zh, xr[4 * d + 3], a, false);
   }
-  return (a0 + a1) + (b0 + b1);
+  return a;
 }
 
 // Position of bulk channel j in the LDS group slots.
