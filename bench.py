@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--chunk-mib", type=int, default=8, help="load: staging chunk size")
     ap.add_argument("--context", type=int, default=8192, help="kv: cached tokens attended per step")
     ap.add_argument("--M", type=int, default=1)
-    ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "mfma"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "gemv", "mfma", "mfma_splitk", "mfma_tiled", "mfma_strip"])
     ap.add_argument("--mode", default="graph", choices=["step", "graph"],
                     help="cfg2/cfg3 at M = 1: a graph of 144 launches, or one persistent launch per step")
     ap.add_argument("--layers", type=int, default=None, help="cfg3: fewer layers (quick runs)")

@@ -531,21 +531,40 @@ namespace {
 // The kernel a product of M rows runs with the selector, or a status < 0
 // (message set).  The container must be live and M and kernel in range.
 int plan_of(const DeviceView& v, int64_t M, int kernel) {
-  // auto: the GEMV for M <= 2, and for M = 3, 4 where the tiled MFMA kernel
-  // declines the shape (measured: the tiled kernel is faster from M = 3 on)
-  const bool auto_gemv = gemv_supports(v, M) && (M <= 2 || !mfma_tiled_supports(v, M));
+  // auto: the GEMV for M <= 2; from M = 3 the split-K MFMA kernel up to
+  // M = 16 (past that the strip kernel measured faster), the tiled one where
+  // split-K declines, else the strip kernel; the GEMV again at M = 3, 4 where
+  // only the strip kernel would take the shape
+  const bool splitk = mfma_splitk_supports(v, M), tiled = mfma_tiled_supports(v, M);
+  const bool split_first = splitk && M <= 16;
+  const bool auto_gemv = gemv_supports(v, M) && (M <= 2 || (!split_first && !tiled));
   if (kernel == SPECTRA_KERNEL_GEMV || (kernel == SPECTRA_KERNEL_AUTO && auto_gemv)) {
     if (!gemv_supports(v, M)) return fail(SPECTRA_E_UNSUPPORTED, "GEMV kernel cannot run this shape");
     return SPECTRA_PLAN_GEMV;
   }
   if (!mfma_supports(v, M)) return fail(SPECTRA_E_UNSUPPORTED, "MFMA kernel cannot run this shape");
-  return mfma_tiled_supports(v, M) ? SPECTRA_PLAN_MFMA_TILED : SPECTRA_PLAN_MFMA;
+  switch (kernel) {
+    case SPECTRA_KERNEL_MFMA_SPLITK:
+      if (!splitk) return fail(SPECTRA_E_UNSUPPORTED, "split-K MFMA kernel cannot run this shape");
+      return SPECTRA_PLAN_MFMA_SPLITK;
+    case SPECTRA_KERNEL_MFMA_TILED:
+      if (!tiled) return fail(SPECTRA_E_UNSUPPORTED, "tiled MFMA kernel cannot run this shape");
+      return SPECTRA_PLAN_MFMA_TILED;
+    case SPECTRA_KERNEL_MFMA_STRIP:
+      return SPECTRA_PLAN_MFMA;
+    default:
+      return split_first ? SPECTRA_PLAN_MFMA_SPLITK : (tiled ? SPECTRA_PLAN_MFMA_TILED : SPECTRA_PLAN_MFMA);
+  }
+}
+
+size_t workspace_of(const DeviceView& v, int64_t M, int plan) {
+  return plan == SPECTRA_PLAN_MFMA_SPLITK ? mfma_splitk_workspace_bytes(v, M) : mfma_workspace_bytes(v, M);
 }
 
 int check_gemm_args(const spectra_container* c, int64_t M, int kernel) {
   if (!c) return fail(SPECTRA_E_INVAL, "invalid or freed container");
   if (M < 1 || M > SPECTRA_MAX_M) return fail(SPECTRA_E_INVAL, "M out of range [1, 2^20]");
-  if (kernel < SPECTRA_KERNEL_AUTO || kernel > SPECTRA_KERNEL_MFMA)
+  if (kernel < SPECTRA_KERNEL_AUTO || kernel > SPECTRA_KERNEL_MFMA_SPLITK)
     return fail(SPECTRA_E_INVAL, "unknown kernel selector");
   return SPECTRA_OK;
 }
@@ -579,9 +598,9 @@ int spectra_gemm_ex(const spectra_container* h, const void* x, void* y, int64_t 
     e = launch_gemv(v, xp, yp, M, s);
   } else {
     void* ws = nullptr;
-    e = stream_workspace(c->device, s, mfma_workspace_bytes(v, M), &ws);
+    e = stream_workspace(c->device, s, workspace_of(v, M, plan), &ws);
     if (e != hipSuccess) return fail(SPECTRA_E_NOMEM, hip_msg("MFMA workspace", e));
-    e = launch_mfma_ws(v, xp, yp, M, ws, s);
+    e = launch_mfma_ws(v, xp, yp, M, ws, s, plan);
   }
   if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("kernel launch", e));
   return SPECTRA_OK;
@@ -608,13 +627,19 @@ int spectra_gemm_noalloc(const spectra_container* h, const void* x, void* y, int
   if (plan == SPECTRA_PLAN_GEMV) {
     e = launch_gemv(v, xp, yp, M, s);  // no workspace
   } else {
-    const size_t need = mfma_workspace_bytes(v, M);
+    // the split-K kernel's partial sums may not fit the scratch: then, unless
+    // it was forced, the kernel it replaces, whose workspace is x alone
+    int run = plan;
+    if (run == SPECTRA_PLAN_MFMA_SPLITK && kernel != SPECTRA_KERNEL_MFMA_SPLITK &&
+        mfma_splitk_workspace_bytes(v, M) > kScratchBytes)
+      run = mfma_tiled_supports(v, M) ? SPECTRA_PLAN_MFMA_TILED : SPECTRA_PLAN_MFMA;
+    const size_t need = workspace_of(v, M, run);
     if (need > kScratchBytes)
       return fail(SPECTRA_E_UNSUPPORTED, "the product needs " + std::to_string(need) +
                                              " bytes of workspace, more than the 8 MiB static scratch");
     void* ws = nullptr;
     if ((e = scratch_on(c->device, &ws)) != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("static scratch address", e));
-    e = launch_mfma_ws(v, xp, yp, M, ws, s);
+    e = launch_mfma_ws(v, xp, yp, M, ws, s, run);
   }
   if (e != hipSuccess) return fail(SPECTRA_E_HIP, hip_msg("kernel launch", e));
   return SPECTRA_OK;

@@ -39,6 +39,7 @@
 // heavy-tailed columns follow as plain MFMA steps (fp16 weights, scale 1).
 // Loads use buffer descriptors: rows past N or M and positions past the
 // padded K read as zero.
+#include "../../include/spectra.h"
 #include "spectra_internal.h"
 
 namespace spectra {
@@ -667,7 +668,372 @@ __global__ __launch_bounds__(kKsThreads) void k_mfma_ks(const DeviceView v, cons
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_mfma_sk: the batched product for 1 <= M <= 32 with K split into ranges
+// of KR = 8 WG groups.  The other kernels stream a few records of many rows
+// per load instruction (16 rows x 64 bytes, or 8 rows x 128 bytes), and this
+// chip's memory system serves those at 4.0 - 4.9 TB/s where one row's 1 KB
+// per instruction streams at 6 TB/s.  Here block b takes K-range s = b % S
+// and walks 16-row tiles t = b / S, b / S + B / S, ...; consecutive blocks
+// read the ranges of one tile, so the chip still streams one moving window
+// of the code section.  Each wave moves two rows of a tile per step into an
+// LDS ring by LDS-DMA, one instruction per row (KR records, <= 1 KB), plus
+// the two rows' scales and zero bytes; the ring holds R tiles, R - 2 of them
+// in flight.  Wave w keeps x of its WG groups (all 16 MT rows) as MFMA A
+// operands in registers for the whole launch, so x is read from memory once
+// per block and never passes through LDS.  Per group: lane (r, c) reads word
+// r of row c's record from the tile, dequantizes it to exact fp16 (q - z),
+// one MFMA per m-subtile into a zero accumulator, and adds it with the
+// group's fp32 scale (the exact form of k_mfma_ks).  The waves' 16 x 16 MT
+// partials of a tile are summed through LDS in fixed order and stored as
+// fp32 to the workspace, P[s][m][n]; k_sk_sum adds the S ranges in order and
+// the heavy-tailed columns.
+constexpr int kSkWaves = 16;  // 4 per SIMD: the LDS -> MFMA -> FMA chains of one hide behind the others
+constexpr int kSkThreads = 64 * kSkWaves;
+constexpr int kSkRow = 1040;   // LDS bytes per code row of a tile: 1 KB of DMA + 16 of pad (rows 4 banks apart)
+constexpr int kSkCodes = 16 * kSkRow;
+constexpr int kSkSRow = 136;   // per scale row: the 33 dwords holding its KR scales + 1 of pad (34 banks apart)
+constexpr int kSkScales = 16 * kSkSRow;
+constexpr int kSkZWave = 48;   // per wave: its row's 10 dwords of zero bytes + 2 of pad (rows 12 banks apart)
+constexpr int kSkZeros = kSkWaves * kSkZWave;
+constexpr int kSkSlot = kSkCodes + kSkScales + kSkZeros;
+constexpr int kSkDma = 3;      // DMA instructions per wave and tile
+template <int MT>
+constexpr int sk_ring() {
+  return MT == 1 ? 6 : 4;
+}
+template <int MT>
+constexpr size_t sk_lds_bytes() {
+  return (size_t)sk_ring<MT>() * kSkSlot + 2 * kSkWaves * MT * 1024;
+}
+
+// One 4-byte LDS-DMA instruction: active lane l's dword at `off` lands at
+// lds + 4 l (inactive lanes write nothing).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t off) {
+  uint32_t save;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(off), "s"(r)
+      : "memory");
+}
+
+// dma16 with the non-temporal hint (code records are read once).
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t off) {
+  uint32_t save;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(off), "s"(r)
+      : "memory");
+}
+
+__host__ __device__ constexpr uint64_t round4(uint64_t b) { return (b + 3) & ~(uint64_t)3; }
+
+template <int MT>
+struct SkAcc {
+  float4_t a[MT];
+};
+
+template <int MT, int WG>
+__global__ __launch_bounds__(kSkThreads) void k_mfma_sk(const DeviceView v, const uint16_t* __restrict__ xw,
+                                                        int KW, int M, int S, float* __restrict__ P) {
+  constexpr int KR = kSkWaves * WG;
+  constexpr int R = sk_ring<MT>();
+  constexpr int D = R - 1;  // tiles in flight while one is computed
+  static_assert(WG >= 1 && WG <= 4, "groups per wave");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r4 = lane >> 4, c = lane & 15;
+  const int G = v.G;
+  const int64_t N = v.N;
+  const int s = (int)(blockIdx.x % (unsigned)S);
+  const int64_t Bs = gridDim.x / S;
+  const int64_t ntiles = (N + 15) / 16;
+  const int g0 = KR * s;
+  const int gw = g0 + WG * w;  // this wave's first group
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(smem);
+  float4_t* part = reinterpret_cast<float4_t*>(smem + R * kSkSlot);  // [2][waves][MT][64]
+  const uint64_t NG = (uint64_t)N * (uint64_t)G;
+  const __amdgpu_buffer_rsrc_t rc = rsrc(v.codes, NG * 16);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(v.scales, round4(NG * 2));
+  const __amdgpu_buffer_rsrc_t rz = rsrc(v.zeros, round4((NG + 1) / 2));
+
+  // Tile t into ring slot `slot`: this wave's rows 2w and 2w + 1 (the row
+  // index is wave-uniform, so the offsets are a scalar base plus the lane).
+  // Every wave issues kSkDma instructions per tile, past the last tile too
+  // (all lanes out of range), so the wait counts are the same on every path.
+  // Offsets fit 31 bits (the launcher checks N G 16).
+  auto issue = [&](int64_t t, int slot) {
+    const uint32_t base = lds0 + (uint32_t)(slot * kSkSlot);
+    const int64_t r0 = t * 16 + w;
+    const bool ok0 = t < ntiles && r0 < N;
+    const uint32_t f0 = (uint32_t)(r0 * G + g0);
+    const bool lc = lane < KR && g0 + lane < G;
+    dma16_nt(rc, base + (uint32_t)(w * kSkRow), ok0 && lc ? (f0 + lane) * 16u : kOob);
+    if (lane <= KR / 2) dma4(rs, base + (uint32_t)(kSkCodes + w * kSkSRow), ok0 ? ((f0 >> 1) + lane) * 4u : kOob);
+    if (lane < 10) dma4(rz, base + (uint32_t)(kSkCodes + kSkScales + w * kSkZWave), ok0 ? (((f0 >> 1) & ~3u) + 4u * lane) : kOob);
+  };
+
+  const int64_t t0 = blockIdx.x / S;
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(t0 + d * Bs, d);
+
+  // x of this wave's groups: A operand lane (r, c) = row 16 tm + c, positions
+  // 8r .. 8r + 7 of the group; rows past M and groups past G read zeros.
+  half8 xa[WG][MT];
+  {
+    const __amdgpu_buffer_rsrc_t rx = rsrc(xw, (uint64_t)M * KW * 2);
+#pragma unroll
+    for (int j = 0; j < WG; ++j)
+#pragma unroll
+      for (int tm = 0; tm < MT; ++tm) {
+        const int m = 16 * tm + c, g = gw + j;
+        const bool ok = m < M && g < G;
+        xa[j][tm] = __builtin_bit_cast(
+            half8, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (uint32_t)(m * KW + 32 * g + 8 * r4) * 2u : kOob, 0, 0));
+      }
+    // consume x here, before the loop: the compiler waits for these loads
+    // (and so for the first tiles) once, not inside the loop
+#pragma unroll
+    for (int j = 0; j < WG; ++j)
+#pragma unroll
+      for (int tm = 0; tm < MT; ++tm) asm volatile("" ::"v"(xa[j][tm]));
+  }
+
+  auto compute = [&](int slot, int64_t t) {
+    SkAcc<MT> acc;
+    const unsigned char* base = smem + slot * kSkSlot;
+    const int64_t n0 = (t * 16 + c) * G + g0;  // flat index of the row's first group of the range
+    const int ph = (int)(n0 & 1);
+    const int zq = (int)(n0 & 7) + WG * w;  // this wave's first zero nibble from the row's first dword
+    const int zb = zq >> 1;
+    const unsigned char* zr = base + kSkCodes + kSkScales + c * kSkZWave;
+    const uint32_t z0 = *reinterpret_cast<const uint32_t*>(zr + (zb & ~3));
+    const uint32_t z1 = *reinterpret_cast<const uint32_t*>(zr + (zb & ~3) + 4);
+    const uint32_t z2 = *reinterpret_cast<const uint32_t*>(zr + (zb & ~3) + 8);
+    const uint64_t zz = ((uint64_t)__builtin_amdgcn_alignbyte(z2, z1, (uint32_t)(zb & 3)) << 32 |
+                         __builtin_amdgcn_alignbyte(z1, z0, (uint32_t)(zb & 3))) >> (4 * (zq & 1));  // nibble j: group gw + j
+    const uint16_t* sr = reinterpret_cast<const uint16_t*>(base + kSkCodes + c * kSkSRow) + ph + WG * w;
+    const unsigned char* cr = base + c * kSkRow + WG * w * 16 + 4 * r4;
+#pragma unroll
+    for (int tm = 0; tm < MT; ++tm) acc.a[tm] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < WG; ++j) {
+      if (gw + j >= G) break;  // wave-uniform: the last range may be partial
+      const uint32_t wd = *reinterpret_cast<const uint32_t*>(cr + 16 * j);
+      const half8 b = dequant_word(wd, (uint32_t)(zz >> (4 * j)) & 0xFu);
+      const float sc = h2f(sr[j]);
+#pragma unroll
+      for (int tm = 0; tm < MT; ++tm) {
+        const float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[j][tm], b, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        acc.a[tm] += sc * p;
+      }
+    }
+    return acc;
+  };
+
+  // Tile t's sum over the waves (partials in part[buf]); D lane (r, c) held
+  // rows 16 tm + 4r + i of output column c.
+  auto store = [&](int64_t t, int buf) {
+    const float4_t* pb = part + buf * kSkWaves * MT * 64;
+    for (int e = tid; e < 16 * M; e += kSkThreads) {
+      const int m = e >> 4, n = e & 15;
+      const int tm = m >> 4, mr = m & 15;
+      const float* pf = reinterpret_cast<const float*>(pb + tm * 64 + (mr >> 2) * 16 + n) + (mr & 3);
+      float sum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kSkWaves; ++ww) sum += pf[ww * MT * 64 * 4];
+      const int64_t row = t * 16 + n;
+      if (row < N) P[((int64_t)s * M + m) * N + row] = sum;
+    }
+  };
+
+  // Iteration it: tile t lands (this wave's part, then every wave's at the
+  // barrier, which also means every wave is done with tile t - 1), tile
+  // t + D goes into t - 1's slot, the previous tile's sums are stored, and
+  // tile t is multiplied into part[it & 1].
+  int64_t t = t0, prev = -1;
+  int it = 0;
+  for (; t < ntiles; t += Bs, ++it) {
+    vm_wait<kSkDma * (D - 1)>();  // this wave's part of tile t has landed
+    lds_barrier();
+    issue(t + D * Bs, (it + D) % R);
+    if (prev >= 0) store(prev, (it - 1) & 1);
+    const SkAcc<MT> acc = compute(it % R, t);
+#pragma unroll
+    for (int tm = 0; tm < MT; ++tm) part[((it & 1) * kSkWaves + w) * MT * 64 + tm * 64 + lane] = acc.a[tm];
+    prev = t;
+  }
+  vm_wait<0>();
+  lds_barrier();
+  if (prev >= 0) store(prev, (it - 1) & 1);
+}
+
+// y = the sum of the S range partials (in range order) plus the heavy-tailed
+// columns: a block of 256 threads takes 64 rows, stages their fp16 outlier
+// weights (one contiguous stretch of the section, 16-byte loads issued
+// together) and the M rows of heavy-tailed x in LDS, and thread (n, q) writes
+// rows m = q, q + 4, ... of output column n.
+constexpr int kSumRows = 64;
+constexpr int kSumThreads = 256;
+constexpr int kSkMaxOut = 256;  // heavy-tailed columns k_sk_sum stages (LDS)
+constexpr int kSkMaxM = 32;
+constexpr int kSumLoads = (kSumRows * kSkMaxOut * 2 + 16 + 16 * kSumThreads - 1) / (16 * kSumThreads);
+constexpr int kSumXLoads = kSkMaxM * (kSkMaxOut / 8) / kSumThreads;
+
+template <int MI>
+__global__ __launch_bounds__(kSumThreads) void k_sk_sum(const DeviceView v, const uint16_t* __restrict__ xw, int KW,
+                                                        int M, int S, const float* __restrict__ P,
+                                                        uint16_t* __restrict__ y) {
+  __shared__ __align__(16) unsigned char ob[kSumLoads * 16 * kSumThreads];
+  __shared__ __align__(16) uint16_t xo[kSkMaxM * kSkMaxOut];
+  const int tid = threadIdx.x;
+  const int n_out = v.n_out, KP = 32 * v.G;
+  const int XS = (n_out + 7) & ~7;  // LDS row stride of heavy-tailed x, halves
+  const int64_t N = v.N;
+  const int64_t n0 = (int64_t)blockIdx.x * kSumRows;
+  const int rows = (int)((N - n0) < kSumRows ? (N - n0) : kSumRows);
+  const int nl = tid & (kSumRows - 1), q = tid / kSumRows;
+  const int64_t n = n0 + (nl < rows ? nl : 0);
+  // rows m = q + 4 i of x, i < MI; rows past M compute on row 0 and are not stored
+  int mrow[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) mrow[i] = q + 4 * i < M ? q + 4 * i : 0;
+  // the ranges four at a time, every load of a round issued before its adds;
+  // round 0 goes out before the staging below
+  float pv[MI][4];
+  auto load_round = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k = k0 + kk < S ? k0 + kk : k0;
+        const float p = P[((int64_t)k * M + mrow[i]) * N + n];
+        pv[i][kk] = k0 + kk < S ? p : 0.f;
+      }
+  };
+  load_round(0);
+  int oh = 0;  // halves from ob's start to row n0's first weight
+  if (n_out > 0) {
+    const uint64_t sec = 2ull * (uint64_t)N * (uint64_t)n_out;
+    const __amdgpu_buffer_rsrc_t ro = rsrc(v.outliers, (sec + 15) & ~15ull);  // sections are 256-byte padded
+    const uint64_t b0 = 2ull * (uint64_t)n0 * (uint64_t)n_out, e0 = b0 + 2ull * (uint64_t)rows * (uint64_t)n_out;
+    const uint64_t a0 = b0 & ~15ull;
+    oh = (int)((b0 - a0) >> 1);
+    u32x4 t[kSumLoads];
+#pragma unroll
+    for (int i = 0; i < kSumLoads; ++i) {
+      const uint64_t off = a0 + 16ull * (uint64_t)(tid + kSumThreads * i);
+      t[i] = __builtin_amdgcn_raw_buffer_load_b128(ro, off < e0 ? (uint32_t)off : kOob, 0, 0);
+    }
+    const int nv = XS / 8;  // 16-byte vectors per row of heavy-tailed x
+    const __amdgpu_buffer_rsrc_t rx = rsrc(xw, (uint64_t)M * KW * 2);
+    u32x4 u[kSumXLoads];
+#pragma unroll
+    for (int i = 0; i < kSumXLoads; ++i) {
+      const int e = tid + kSumThreads * i, m = e / nv, k = e - m * nv;
+      u[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, m < M ? (uint32_t)((m * KW + KP) * 2 + 16 * k) : kOob, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kSumLoads; ++i) *reinterpret_cast<u32x4*>(ob + 16 * (tid + kSumThreads * i)) = t[i];
+#pragma unroll
+    for (int i = 0; i < kSumXLoads; ++i) {
+      const int e = tid + kSumThreads * i, m = e / nv, k = e - m * nv;
+      if (m < M) *reinterpret_cast<u32x4*>(xo + m * XS + 8 * k) = u[i];
+    }
+  }
+  __syncthreads();
+  if (nl >= rows) return;
+  float acc[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) acc[i] = 0.f;
+  for (int k0 = 0; k0 < S; k0 += 4) {
+    if (k0 > 0) load_round(k0);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc[i] += pv[i][kk];
+  }
+  const uint16_t* orow = reinterpret_cast<const uint16_t*>(ob) + oh + nl * n_out;
+  int j = 0;
+  for (; j + 4 <= n_out; j += 4) {
+    float o[4], xv[MI][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = h2f(orow[j + u]);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) xv[i][u] = h2f(xo[mrow[i] * XS + j + u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < MI; ++i) acc[i] += xv[i][u] * o[u];
+  }
+  for (; j < n_out; ++j) {
+    const float o = h2f(orow[j]);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) acc[i] += h2f(xo[mrow[i] * XS + j]) * o;
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+    if (q + 4 * i < M) y[(int64_t)(q + 4 * i) * N + n] = f2h(acc[i]);
+}
+
 }  // namespace
+
+namespace {
+
+struct SkShape {
+  int S, WG;  // K-ranges, groups per wave (a range is 8 WG groups)
+};
+SkShape sk_shape(const DeviceView& v) {
+  const int S = (v.G + 63) / 64;
+  const int per = (v.G + S - 1) / S;
+  return SkShape{S, (per + 15) / 16};
+}
+
+size_t ks_lds_limit(const DeviceView& v);
+
+template <int MT>
+bool sk_fits(const DeviceView& v) {
+  return sk_lds_bytes<MT>() <= ks_lds_limit(v);
+}
+
+size_t sk_x_bytes(const DeviceView& v, int64_t M) {
+  const int64_t KW = 32 * (int64_t)v.G + ((v.n_out + 31) & ~31);
+  return ((size_t)(M * KW * 2) + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+// The split-K kernel: 1 <= M <= 32, at most 256 heavy-tailed columns
+// (k_sk_sum stages them in LDS), code and outlier section offsets within 31
+// bits.
+bool mfma_splitk_supports(const DeviceView& v, int64_t M) {
+  if (M < 1 || M > kSkMaxM || v.N < 1) return false;
+  if (v.G < 1 || v.n_out > kSkMaxOut) return false;
+  if ((uint64_t)v.N * (uint64_t)v.G * 16 >= 0x7FFFFFFFull) return false;
+  if ((uint64_t)v.N * (uint64_t)v.n_out * 2 >= 0x7FFFFFF0ull) return false;
+  const int64_t KW = 32 * (int64_t)v.G + ((v.n_out + 31) & ~31);
+  if (M * KW * 2 >= 0x7FFFFFFF) return false;
+  return M <= 16 ? sk_fits<1>(v) : sk_fits<2>(v);
+}
+
+size_t mfma_splitk_workspace_bytes(const DeviceView& v, int64_t M) {
+  return sk_x_bytes(v, M) + (size_t)sk_shape(v).S * (size_t)M * (size_t)v.N * 4;
+}
 
 bool mfma_supports(const DeviceView& v, int64_t M) {
   // workspace row must stay addressable with 32-bit byte offsets per block
@@ -784,6 +1150,52 @@ hipError_t launch_ks(const DeviceView& v, const uint16_t* xw, int KW, int64_t M,
   }
 }
 
+template <int MT, int WG>
+hipError_t launch_sk_wg(const DeviceView& v, const uint16_t* xw, int KW, int64_t M, float* P, hipStream_t s,
+                        int S) {
+  constexpr size_t lds = sk_lds_bytes<MT>();
+  const void* fn = reinterpret_cast<const void*>(&k_mfma_sk<MT, WG>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t cu = v.cu_count > 0 ? v.cu_count : 1;
+  const int64_t tiles = (v.N + 15) / 16;
+  int64_t bs = cu / S;  // blocks per K-range: one block per compute unit in all
+  if (bs < 1) bs = 1;
+  if (bs > tiles) bs = tiles;
+  hipLaunchKernelGGL((k_mfma_sk<MT, WG>), dim3((unsigned)(bs * S)), dim3(kSkThreads), lds, s, v, xw, KW, (int)M, S, P);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_sk_mt(const DeviceView& v, const uint16_t* xw, int KW, int64_t M, float* P, hipStream_t s) {
+  const SkShape sh = sk_shape(v);
+  switch (sh.WG) {
+    case 1: return launch_sk_wg<MT, 1>(v, xw, KW, M, P, s, sh.S);
+    case 2: return launch_sk_wg<MT, 2>(v, xw, KW, M, P, s, sh.S);
+    case 3: return launch_sk_wg<MT, 3>(v, xw, KW, M, P, s, sh.S);
+    case 4: return launch_sk_wg<MT, 4>(v, xw, KW, M, P, s, sh.S);
+    default: return hipErrorNotSupported;
+  }
+}
+
+hipError_t launch_sk(const DeviceView& v, const uint16_t* xw, int KW, int64_t M, uint16_t* y, void* workspace,
+                     hipStream_t s) {
+  float* P = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + sk_x_bytes(v, M));
+  const hipError_t e = M <= 16 ? launch_sk_mt<1>(v, xw, KW, M, P, s) : launch_sk_mt<2>(v, xw, KW, M, P, s);
+  if (e != hipSuccess) return e;
+  const unsigned blocks = (unsigned)((v.N + kSumRows - 1) / kSumRows);
+  const int S = sk_shape(v).S;
+  if (M <= 4)
+    hipLaunchKernelGGL(k_sk_sum<1>, dim3(blocks), dim3(kSumThreads), 0, s, v, xw, KW, (int)M, S, P, y);
+  else if (M <= 8)
+    hipLaunchKernelGGL(k_sk_sum<2>, dim3(blocks), dim3(kSumThreads), 0, s, v, xw, KW, (int)M, S, P, y);
+  else if (M <= 16)
+    hipLaunchKernelGGL(k_sk_sum<4>, dim3(blocks), dim3(kSumThreads), 0, s, v, xw, KW, (int)M, S, P, y);
+  else
+    hipLaunchKernelGGL(k_sk_sum<8>, dim3(blocks), dim3(kSumThreads), 0, s, v, xw, KW, (int)M, S, P, y);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool mfma_tiled_supports(const DeviceView& v, int64_t M) {
@@ -791,13 +1203,14 @@ bool mfma_tiled_supports(const DeviceView& v, int64_t M) {
 }
 
 hipError_t launch_mfma_ws(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M,
-                          void* workspace, hipStream_t s) {
+                          void* workspace, hipStream_t s, int plan) {
   const int KW = 32 * v.G + ((v.n_out + 31) & ~31);
   uint16_t* xw = static_cast<uint16_t*>(workspace);
   const unsigned gy = (unsigned)(M < 65535 ? M : 65535);
   hipLaunchKernelGGL(k_xbulk, dim3((unsigned)((KW + kThreads - 1) / kThreads), gy),
                      dim3(kThreads), 0, s, v, x, M, xw, KW);
-  if (ks_supports(v, KW, M)) return launch_ks(v, xw, KW, M, y, s);
+  if (plan == SPECTRA_PLAN_MFMA_SPLITK) return launch_sk(v, xw, KW, M, y, workspace, s);
+  if (plan == SPECTRA_PLAN_MFMA_TILED) return launch_ks(v, xw, KW, M, y, s);
   if (M <= 16) return launch_mt<1>(v, xw, KW, M, y, s);
   if (M <= 32) return launch_mt<2>(v, xw, KW, M, y, s);
   if (M <= 64) return launch_mt<4>(v, xw, KW, M, y, s);

@@ -132,10 +132,17 @@ hipError_t launch_gemv_grouped(const DeviceView* vs, int count, const uint16_t* 
 bool mfma_supports(const DeviceView& v, int64_t M);
 // The MFMA path runs the shape on its 16-row tiled kernel (k_mfma_ks).
 bool mfma_tiled_supports(const DeviceView& v, int64_t M);
-// Device workspace the MFMA path needs for M input rows (x permuted to bulk order).
+// The MFMA path runs the shape on its split-K kernel (k_mfma_sk + k_sk_sum).
+bool mfma_splitk_supports(const DeviceView& v, int64_t M);
+// Device workspace the MFMA path needs for M input rows: x permuted to bulk
+// order, and for the split-K kernel the fp32 partial sums of every K-range.
 size_t mfma_workspace_bytes(const DeviceView& v, int64_t M);
+size_t mfma_splitk_workspace_bytes(const DeviceView& v, int64_t M);
+// plan: SPECTRA_PLAN_MFMA_SPLITK (the workspace holds
+// mfma_splitk_workspace_bytes), SPECTRA_PLAN_MFMA_TILED or SPECTRA_PLAN_MFMA,
+// each on a shape its supports test accepts.
 hipError_t launch_mfma_ws(const DeviceView& v, const uint16_t* x, uint16_t* y, int64_t M,
-                          void* workspace, hipStream_t s);
+                          void* workspace, hipStream_t s, int plan);
 
 // ---- row gather (embed.hip) ----
 bool embed_supports(const DeviceView& v);

@@ -23,7 +23,7 @@ SPECTRA_E_UNSUPPORTED = -5
 SPECTRA_E_IO = -6
 SPECTRA_E_TIMEOUT = -7
 
-KERNELS = {"auto": 0, "gemv": 1, "mfma": 2}
+KERNELS = {"auto": 0, "gemv": 1, "mfma": 2, "mfma_tiled": 3, "mfma_strip": 4, "mfma_splitk": 5}
 
 EXPORTED = ["spectra_pack", "spectra_pack_device", "spectra_gemm", "spectra_gemm_ex", "spectra_gemm_noalloc",
             "spectra_gemm_plan",
@@ -265,7 +265,7 @@ def spectra_gemm_noalloc(c: Container, x, y, stream=None, kernel: str = "auto"):
     return y
 
 
-PLANS = {1: "k_gemv_m1", 2: "k_mfma_ks", 3: "k_mfma"}
+PLANS = {1: "k_gemv_m1", 2: "k_mfma_ks", 3: "k_mfma", 4: "k_mfma_sk"}
 
 
 def spectra_gemm_plan(c: Container, M: int, kernel: str = "auto") -> str:

@@ -123,13 +123,20 @@ typedef enum {
 
 /* Kernel selection for spectra_gemm_ex. */
 typedef enum {
-  SPECTRA_KERNEL_AUTO = 0,     /* GEMV for M <= 2 (M <= 4 where the tiled MFMA kernel declines the
-                                  shape) if it supports the shape, MFMA otherwise */
-  SPECTRA_KERNEL_GEMV = 1,     /* VALU dequant-GEMV, x in LDS, fp32 accumulate; M <= 4, and
-                                  K % 8 == 0 when M > 1 (else SPECTRA_E_UNSUPPORTED) */
-  SPECTRA_KERNEL_MFMA = 2      /* register-dequantized (q - z) tiles on v_mfma_f32_16x16x32_f16:
-                                  16-row tiles with K split over 8 waves when M <= 16 and the M rows
-                                  of x fit in LDS, one 16-row strip per wave otherwise */
+  SPECTRA_KERNEL_AUTO = 0,        /* GEMV for M <= 2 (M <= 4 where no MFMA kernel but the strip
+                                     kernel takes the shape) if it supports the shape, else as
+                                     SPECTRA_KERNEL_MFMA */
+  SPECTRA_KERNEL_GEMV = 1,        /* VALU dequant-GEMV, x in LDS, fp32 accumulate; M <= 4, and
+                                     K % 8 == 0 when M > 1 (else SPECTRA_E_UNSUPPORTED) */
+  SPECTRA_KERNEL_MFMA = 2,        /* the split-K kernel below for M <= 16 where it takes the shape,
+                                     else the tiled kernel where it does, else the strip kernel */
+  SPECTRA_KERNEL_MFMA_TILED = 3,  /* 16-row tiles with K split over 8 waves: M <= 16, the M rows of
+                                     x in LDS */
+  SPECTRA_KERNEL_MFMA_STRIP = 4,  /* one 16-row strip per wave for the whole K loop: any shape the
+                                     MFMA path takes */
+  SPECTRA_KERNEL_MFMA_SPLITK = 5  /* K split in ranges over blocks, x of a range held in registers,
+                                     fp32 partial sums in the workspace: M <= 32, an even number of
+                                     32-member groups per row, at most 256 heavy-tailed columns */
 } spectra_kernel;
 
 typedef struct {
@@ -179,14 +186,17 @@ int spectra_gemm_ex(const spectra_container* c, const void* x, void* y, int64_t 
 /* spectra_gemm_ex for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation):
  * the same product and kernels, bit for bit, but the MFMA path's workspace
- * (x permuted to bulk order, M * (32 G + n_out rounded up to 32) * 2 bytes)
+ * (x permuted to bulk order, M * (32 G + n_out rounded up to 32) * 2 bytes,
+ * plus for the split-K kernel 4 * M * N bytes of partial sums per K-range)
  * is a static 8 MiB device array of the library instead of the per-stream
- * workspace, and the call makes no device allocation at all.  The
- * container's device must be the current device (E_INVAL otherwise); a
- * product whose workspace exceeds 8 MiB returns SPECTRA_E_UNSUPPORTED and
- * enqueues nothing.  Every call on one GPU shares that GPU's array: calls
- * that overlap on one GPU (other streams, other threads) race and must be
- * serialized by the caller. */
+ * workspace, and the call makes no device allocation at all.  Where the
+ * split-K kernel's workspace exceeds 8 MiB and that kernel was not forced,
+ * the MFMA kernel it replaces runs instead (same bound, not bit-equal to
+ * spectra_gemm_ex).  The container's device must be the current device
+ * (E_INVAL otherwise); a product whose workspace still exceeds 8 MiB
+ * returns SPECTRA_E_UNSUPPORTED and enqueues nothing.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialized by the caller. */
 int spectra_gemm_noalloc(const spectra_container* c, const void* x, void* y, int64_t M,
                          void* stream, int kernel);
 
@@ -194,14 +204,16 @@ int spectra_gemm_noalloc(const spectra_container* c, const void* x, void* y, int
  * `kernel` (a spectra_kernel), without any device work: the product is the
  * fused dequantize-and-multiply of spectra_gemm (SPECTRA page, abstract and
  * highlight 4); this only reports how it would be launched.  Returns
- * SPECTRA_PLAN_GEMV, SPECTRA_PLAN_MFMA_TILED or SPECTRA_PLAN_MFMA; or, as
+ * SPECTRA_PLAN_GEMV, SPECTRA_PLAN_MFMA_TILED, SPECTRA_PLAN_MFMA or
+ * SPECTRA_PLAN_MFMA_SPLITK; or, as
  * spectra_gemm_ex would, SPECTRA_E_INVAL (invalid container, M out of range,
  * unknown selector) or SPECTRA_E_UNSUPPORTED (a forced kernel that cannot run
  * the shape). */
 enum {
   SPECTRA_PLAN_GEMV = 1,        /* k_gemv_m1: VALU dequant-GEMV */
   SPECTRA_PLAN_MFMA_TILED = 2,  /* k_xbulk + k_mfma_ks: 16-row tiles, K split over 8 waves */
-  SPECTRA_PLAN_MFMA = 3         /* k_xbulk + k_mfma: one 16-row strip per wave */
+  SPECTRA_PLAN_MFMA = 3,        /* k_xbulk + k_mfma: one 16-row strip per wave */
+  SPECTRA_PLAN_MFMA_SPLITK = 4  /* k_xbulk + k_mfma_sk + k_sk_sum: K split in ranges, fp32 partials */
 };
 int spectra_gemm_plan(const spectra_container* c, int64_t M, int kernel);
 

@@ -55,8 +55,8 @@ def test_status_codes_match_header():
     kernels = dict(re.findall(r"SPECTRA_KERNEL_(\w+)\s*=\s*(\d+)", text))
     assert {k.lower(): int(v) for k, v in kernels.items()} == sp.KERNELS
     plans = {int(v): k for k, v in re.findall(r"SPECTRA_PLAN_(\w+)\s*=\s*(\d+)", text)}
-    assert plans == {1: "GEMV", 2: "MFMA_TILED", 3: "MFMA"}
-    assert sp.PLANS == {1: "k_gemv_m1", 2: "k_mfma_ks", 3: "k_mfma"}
+    assert plans == {1: "GEMV", 2: "MFMA_TILED", 3: "MFMA", 4: "MFMA_SPLITK"}
+    assert sp.PLANS == {1: "k_gemv_m1", 2: "k_mfma_ks", 3: "k_mfma", 4: "k_mfma_sk"}
 
 
 def test_host_argument_checks_without_a_device():

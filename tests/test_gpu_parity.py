@@ -379,9 +379,11 @@ def test_grouped_launch_chunks_and_mixed_lengths():
 
 def test_kernel_plan_follows_the_selection_rule():
     """spectra_gemm_plan names what spectra_gemm_ex runs: the GEMV up to M = 2,
-    the tiled MFMA kernel from M = 3 where it runs the shape, the GEMV again at
-    M = 3, 4 where it does not (here: more than 16 heavy-tailed blocks), and
-    k_mfma past both (here: more groups per row than either holds)."""
+    the split-K MFMA kernel for 3 <= M <= 16 where it runs the shape and the
+    strip kernel past it; the GEMV again at M = 3, 4 where only the strip
+    kernel would take the shape (here: more heavy-tailed columns than the
+    split-K and tiled kernels stage).  Each MFMA kernel can be forced, and a
+    forced kernel that cannot run the shape is refused."""
     sp = _sp()
     from dequant_gemv_spectra_amd import synth as S
     W, g, _ = S.random_case(100, 4096, 40, 90)
@@ -391,15 +393,23 @@ def test_kernel_plan_follows_the_selection_rule():
     assert O.unpack(img)["n_out"] > 16 * 32
     W, g, _ = S.random_case(40, 15000, 100, 92)
     c15k, _ = check_pack(W, g)
-    assert [sp.spectra_gemm_plan(c4k, M) for M in (1, 2, 3, 4, 8, 16, 17)] == \
-        ["k_gemv_m1"] * 2 + ["k_mfma_ks"] * 4 + ["k_mfma"]
+    assert [sp.spectra_gemm_plan(c4k, M) for M in (1, 2, 3, 4, 8, 16, 17, 32, 33)] == \
+        ["k_gemv_m1"] * 2 + ["k_mfma_sk"] * 4 + ["k_mfma"] * 3
+    assert sp.spectra_gemm_plan(c4k, 32, kernel="mfma_splitk") == "k_mfma_sk"
     assert [sp.spectra_gemm_plan(cout, M) for M in (1, 2, 3, 4, 5)] == ["k_gemv_m1"] * 4 + ["k_mfma"]
-    assert [sp.spectra_gemm_plan(c15k, M) for M in (1, 2, 3, 5)] == ["k_gemv_m1"] * 2 + ["k_mfma"] * 2
+    assert [sp.spectra_gemm_plan(c15k, M) for M in (1, 2, 3, 5, 33)] == ["k_gemv_m1"] * 2 + ["k_mfma_sk"] * 2 + ["k_mfma"]
     assert sp.spectra_gemm_plan(c4k, 3, kernel="gemv") == "k_gemv_m1"
-    assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma") == "k_mfma_ks"
-    with pytest.raises(sp.SpectraError) as ei:
-        sp.spectra_gemm_plan(c4k, 8, kernel="gemv")  # the GEMV takes M <= 4
-    assert ei.value.status == sp.SPECTRA_E_UNSUPPORTED
+    assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma") == "k_mfma_sk"
+    assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma_tiled") == "k_mfma_ks"
+    assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma_strip") == "k_mfma"
+    assert sp.spectra_gemm_plan(cout, 5, kernel="mfma") == "k_mfma"
+    for h, M, kernel in ((c4k, 8, "gemv"),          # the GEMV takes M <= 4
+                         (c4k, 17, "mfma_tiled"),   # the tiled kernel M <= 16
+                         (c4k, 33, "mfma_splitk"),  # the split-K kernel M <= 32
+                         (cout, 3, "mfma_splitk")):  # and at most 256 heavy-tailed columns
+        with pytest.raises(sp.SpectraError) as ei:
+            sp.spectra_gemm_plan(h, M, kernel=kernel)
+        assert ei.value.status == sp.SPECTRA_E_UNSUPPORTED, (M, kernel)
     with pytest.raises(sp.SpectraError) as ei:
         sp.spectra_gemm_plan(c4k, 0)
     assert ei.value.status == sp.SPECTRA_E_INVAL
@@ -505,12 +515,78 @@ MFMA_CASES = [  # (N, K, planted heavy-tailed channels, seed, M)
 ]
 
 
+MFMA_KERNELS = ("mfma_splitk", "mfma_tiled", "mfma_strip")
+
+
+def mfma_kernels_for(c, M):
+    """The MFMA kernels that run M rows of x on container c."""
+    sp = _sp()
+    out = []
+    for k in MFMA_KERNELS:
+        try:
+            sp.spectra_gemm_plan(c, M, kernel=k)
+        except sp.SpectraError as e:
+            assert e.status == sp.SPECTRA_E_UNSUPPORTED
+            continue
+        out.append(k)
+    return out
+
+
 @pytest.mark.parametrize("N,K,n_out,seed,M", MFMA_CASES)
 def test_mfma_product_small(N, K, n_out, seed, M):
     W, g, x = synth.random_case(N, K, n_out, seed, M=M)
     c, img = check_pack(W, g)
     check_product(c, img, x)                   # auto: the MFMA path from M = 3 (and shapes the GEMV declines)
-    check_product(c, img, x, kernel="mfma")
+    kernels = mfma_kernels_for(c, M)
+    assert "mfma_strip" in kernels
+    for k in kernels:
+        check_product(c, img, x, kernel=k)
+
+
+SPLITK_CASES = [  # (N, K, planted heavy-tailed channels, seed, M): groups per row G, K-ranges S, groups per wave WG
+    (100, 1000, 8, 201, 5),     # G 32, S 1, WG 4
+    (77, 2048, 0, 202, 16),     # G 64, S 1, WG 8
+    (130, 2600, 30, 203, 17),   # G 81 (odd: rows start mid-dword), S 2, WG 6, two m-subtiles
+    (45, 520, 5, 204, 1),       # G 17, M = 1
+    (300, 4100, 90, 205, 32),   # G 126, S 2, 78 heavy-tailed columns
+    (64, 8192, 82, 206, 12),    # G 255, S 4
+    (257, 3072, 31, 207, 2),    # G 96, S 2, WG 6
+    (33, 1500, 300, 208, 9),    # 97 heavy-tailed columns, G 44
+    (200, 9728, 150, 209, 7),   # G 301, S 5, last range 45 groups
+    (513, 6000, 60, 210, 24),   # G 186, S 3
+    (40, 12000, 250, 211, 3),   # G 372, S 6
+    (128, 300, 6, 215, 31),     # G 10, WG 2: waves 5 .. 7 have no group
+    (17, 2100, 20, 213, 4),     # G 66, one ragged tile
+]
+
+
+@pytest.mark.parametrize("N,K,n_out,seed,M", SPLITK_CASES)
+def test_splitk_product(N, K, n_out, seed, M):
+    """The split-K kernel against the oracle on every element, and bit-equal
+    on a second run (partial sums are added in a fixed order)."""
+    sp, torch = _sp(), _torch()
+    W, g, x = synth.random_case(N, K, n_out, seed, M=M)
+    c, img = check_pack(W, g)
+    assert sp.spectra_gemm_plan(c, M, kernel="mfma_splitk") == "k_mfma_sk"
+    y1 = check_product(c, img, x, kernel="mfma_splitk")
+    y2 = sp.spectra_gemm(c, torch.from_numpy(x).cuda(), kernel="mfma_splitk").cpu().numpy()
+    assert np.array_equal(y1, y2.astype(np.float64))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("N,K,n_out,seed,M", [(60000, 256, 3, 222, 8), (29000, 2048, 20, 223, 20)])
+def test_splitk_many_tiles_per_block(N, K, n_out, seed, M):
+    """Enough 16-row tiles that every block's LDS ring wraps several times
+    (15 and 7 tiles per block on 256 compute units): every element of the
+    first, sampled rows of the rest."""
+    sp = _sp()
+    W, g, x = synth.random_case(N, K, n_out, seed, M=M)
+    c = sp.spectra_pack(W, g)
+    del W
+    img = sp.spectra_export(c)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([np.arange(4096), rng.integers(0, N, 3000), np.arange(N - 300, N)]))
+    check_product(c, img, x, kernel="mfma_splitk", rows=rows)
 
 
 @pytest.mark.parametrize("M", [6, 24, 40, 128])
@@ -529,7 +605,8 @@ def test_mfma_rows_of_huge_scales(M):
     u = O.unpack(img)
     s = u["s16"].astype(np.float32)
     assert (s[:72].max(axis=1) >= 4096).all() and (s[72:] < 4096).all()
-    check_product(c, img, x, kernel="mfma")
+    for k in mfma_kernels_for(c, M):
+        check_product(c, img, x, kernel=k)
 
 
 WIDE_MFMA = [  # (N, K, planted heavy-tailed channels, seed, M): more 16-row tiles than 7 per compute unit
@@ -551,17 +628,18 @@ def test_mfma_wide_grids(N, K, n_out, seed, M):
     W, g, x = synth.random_case(N, K, n_out, seed, M=M)
     c = sp.spectra_pack(W, g)
     del W
-    assert sp.spectra_gemm_plan(c, M, kernel="mfma") == "k_mfma"
+    assert sp.spectra_gemm_plan(c, M, kernel="mfma_strip") == "k_mfma"
     img = sp.spectra_export(c)
     rng = np.random.default_rng(seed)
     rows = np.unique(np.concatenate([np.arange(2 * 7 * 64), rng.integers(0, N, 2000), np.arange(N - 300, N)]))
-    check_product(c, img, x, kernel="mfma", rows=rows)
+    check_product(c, img, x, kernel="mfma_strip", rows=rows)
 
 
 def test_mfma_at_m1_and_gemv_agree_with_oracle():
     W, g, x = synth.random_case(700, 2560, 30, 41, M=1)
     c, img = check_pack(W, g)
-    check_product(c, img, x, kernel="mfma")
+    for k in mfma_kernels_for(c, 1):
+        check_product(c, img, x, kernel=k)
     check_product(c, img, x, kernel="gemv")
 
 
@@ -575,9 +653,10 @@ def test_mfma_one_hot_columns_exact():
     x = np.zeros((len(ks), 300), np.float16)
     for i, k in enumerate(ks):
         x[i, k] = 1.0
-    y = sp.spectra_gemm(c, torch.from_numpy(x).cuda(), kernel="mfma").cpu().numpy()
-    for i, k in enumerate(ks):
-        assert np.array_equal(y[i], u["W_hat"][:, k].astype(np.float16)), k
+    for kernel in mfma_kernels_for(c, len(ks)):
+        y = sp.spectra_gemm(c, torch.from_numpy(x).cuda(), kernel=kernel).cpu().numpy()
+        for i, k in enumerate(ks):
+            assert np.array_equal(y[i], u["W_hat"][:, k].astype(np.float16)), (kernel, k)
 
 
 @pytest.mark.timeout(900)
@@ -594,9 +673,9 @@ def test_config_large_batched(cfg):
             continue
         x = synth.activations(lin, cfg, M)
         check_product(c, img, x, rows=rows)  # auto
-        if M <= 4:  # both kernels at the same M
-            check_product(c, img, x, rows=rows, kernel="gemv")
-            check_product(c, img, x, rows=rows, kernel="mfma")
+        kernels = mfma_kernels_for(c, M) + (["gemv"] if M <= 4 else [])
+        for k in kernels:  # every kernel that runs the shape
+            check_product(c, img, x, rows=rows, kernel=k)
 
 
 def test_captured_graph_survives_workspace_growth():
