@@ -1,6 +1,7 @@
 // SPECTRA batched product for gfx950: y = x W_hat^T on the matrix cores
 // (v_mfma_f32_16x16x32_f16): automatic from M = 3 on (the GEMV keeps M <= 2,
-// and M <= 4 where the tiled kernel declines), and for shapes the GEMV declines.
+// and M <= 4 where only the strip kernel would take the shape), and for
+// shapes the GEMV declines.
 //
 // The SPECTRA page reports Tensor-Core prefill next to its decode kernels
 // (highlight 4); this is the gfx950 counterpart for batched rows, written for
@@ -10,8 +11,9 @@
 // bulk order, zero padded to 32G, followed by the heavy-tailed x values
 // zero padded to a multiple of 32.
 //
-// Pass 2 is k_mfma_ks (below) when 1 <= M <= 16 and the M rows of x fit in
-// LDS, else k_mfma.
+// Pass 2 is one of three kernels: k_mfma_sk + k_sk_sum (split-K, below;
+// the default for M <= 16 where it takes the shape), k_mfma_ks (16-row tiles
+// with the M rows of x in LDS) or k_mfma (one 16-row strip per wave).
 //
 // k_mfma: a wave owns 16 * NT consecutive output rows for the whole
 // K loop.  Per chunk of CG groups it loads its code records row-contiguously
