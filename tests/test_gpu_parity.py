@@ -379,11 +379,13 @@ def test_grouped_launch_chunks_and_mixed_lengths():
 
 def test_kernel_plan_follows_the_selection_rule():
     """spectra_gemm_plan names what spectra_gemm_ex runs: the GEMV up to M = 2,
-    the split-K MFMA kernel for 3 <= M <= 16 where it runs the shape and the
-    strip kernel past it; the GEMV again at M = 3, 4 where only the strip
-    kernel would take the shape (here: more heavy-tailed columns than the
-    split-K and tiled kernels stage).  Each MFMA kernel can be forced, and a
-    forced kernel that cannot run the shape is refused."""
+    from M = 3 the tiled MFMA kernel where it runs the shape, the split-K
+    kernel up to M = 16 where the tiled one does not (here: more groups per
+    row than the tiled kernel holds), the strip kernel past both; the GEMV
+    again at M = 3, 4 where only the strip kernel would take the shape (here:
+    more heavy-tailed columns than the split-K and tiled kernels stage).  Each
+    MFMA kernel can be forced, and a forced kernel that cannot run the shape
+    is refused."""
     sp = _sp()
     from dequant_gemv_spectra_amd import synth as S
     W, g, _ = S.random_case(100, 4096, 40, 90)
@@ -394,12 +396,14 @@ def test_kernel_plan_follows_the_selection_rule():
     W, g, _ = S.random_case(40, 15000, 100, 92)
     c15k, _ = check_pack(W, g)
     assert [sp.spectra_gemm_plan(c4k, M) for M in (1, 2, 3, 4, 8, 16, 17, 32, 33)] == \
-        ["k_gemv_m1"] * 2 + ["k_mfma_sk"] * 4 + ["k_mfma"] * 3
+        ["k_gemv_m1"] * 2 + ["k_mfma_ks"] * 4 + ["k_mfma"] * 3
     assert sp.spectra_gemm_plan(c4k, 32, kernel="mfma_splitk") == "k_mfma_sk"
+    assert sp.spectra_gemm_plan(c4k, 8, kernel="mfma_splitk") == "k_mfma_sk"
     assert [sp.spectra_gemm_plan(cout, M) for M in (1, 2, 3, 4, 5)] == ["k_gemv_m1"] * 4 + ["k_mfma"]
     assert [sp.spectra_gemm_plan(c15k, M) for M in (1, 2, 3, 5, 33)] == ["k_gemv_m1"] * 2 + ["k_mfma_sk"] * 2 + ["k_mfma"]
     assert sp.spectra_gemm_plan(c4k, 3, kernel="gemv") == "k_gemv_m1"
-    assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma") == "k_mfma_sk"
+    assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma") == "k_mfma_ks"
+    assert sp.spectra_gemm_plan(c15k, 1, kernel="mfma") == "k_mfma_sk"
     assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma_tiled") == "k_mfma_ks"
     assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma_strip") == "k_mfma"
     assert sp.spectra_gemm_plan(cout, 5, kernel="mfma") == "k_mfma"

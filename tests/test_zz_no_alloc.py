@@ -50,9 +50,10 @@ def test_noalloc_refuses_a_workspace_past_its_scratch():
 def test_noalloc_runs_split_k_and_falls_back_past_its_scratch():
     """The split-K kernel under the no-allocation entry point: bit-equal to
     spectra_gemm_ex while its fp32 partial sums fit the 8 MiB scratch; past
-    that (here 2 K-ranges x 16 rows x 70000 outputs x 4 bytes) the entry point
-    runs the MFMA kernel that split-K replaces, within the oracle bound on
-    sampled rows."""
+    that (here 6 K-ranges x 16 rows x 24000 outputs x 4 bytes, on a shape the
+    tiled kernel declines, so that the default runs split-K) the entry point
+    runs the strip kernel instead, within the oracle bound on sampled rows,
+    and refuses split-K when it is forced."""
     import torch
     from dequant_gemv_spectra_amd import spectra as sp
     W, g, _ = synth.random_case(3000, 2048, 20, 125)
@@ -60,28 +61,27 @@ def test_noalloc_runs_split_k_and_falls_back_past_its_scratch():
     W_hat = O.unpack(sp.spectra_export(c))["W_hat"]
     rng = np.random.default_rng(125)
     for M in (8, 3):
-        assert sp.spectra_gemm_plan(c, M) == "k_mfma_sk"
         x = rng.standard_normal((M, 2048)).astype(np.float16)
         xd = torch.from_numpy(x).cuda()
-        y_ref = sp.spectra_gemm(c, xd)
+        y_ref = sp.spectra_gemm(c, xd, kernel="mfma_splitk")
         y = torch.full((M, 3000), 3.0, dtype=torch.float16, device="cuda")
-        sp.spectra_gemm_noalloc(c, xd, y)
+        sp.spectra_gemm_noalloc(c, xd, y, kernel="mfma_splitk")
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref), f"M={M}: differs from spectra_gemm_ex"
         err = np.abs(y.cpu().numpy().astype(np.float64) - O.matmul_ref(W_hat, x))
         assert (err <= O.tolerance(W_hat, x)).all()
     c.close()
-    W, g, _ = synth.random_case(70000, 3072, 31, 126)
+    W, g, _ = synth.random_case(24000, 12000, 100, 126)
     c = sp.spectra_pack(W, g)
     del W
     img = sp.spectra_export(c)
     M = 16
     assert sp.spectra_gemm_plan(c, M) == "k_mfma_sk"
-    x = rng.standard_normal((M, 3072)).astype(np.float16)
-    y = torch.full((M, 70000), 3.0, dtype=torch.float16, device="cuda")
+    x = rng.standard_normal((M, 12000)).astype(np.float16)
+    y = torch.full((M, 24000), 3.0, dtype=torch.float16, device="cuda")
     sp.spectra_gemm_noalloc(c, torch.from_numpy(x).cuda(), y)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.arange(512), rng.integers(0, 70000, 1500), np.arange(69700, 70000)]))
+    rows = np.unique(np.concatenate([np.arange(512), rng.integers(0, 24000, 1500), np.arange(23700, 24000)]))
     W_hat = O.reconstruct_rows(img, rows)
     err = np.abs(y.cpu().numpy()[:, rows].astype(np.float64) - O.matmul_ref(W_hat, x))
     assert (err <= O.tolerance(W_hat, x)).all()
