@@ -531,14 +531,12 @@ namespace {
 // The kernel a product of M rows runs with the selector, or a status < 0
 // (message set).  The container must be live and M and kernel in range.
 int plan_of(const DeviceView& v, int64_t M, int kernel) {
-  // auto: the GEMV for M <= 2; from M = 3 the tiled MFMA kernel where it
-  // takes the shape, else the split-K kernel up to M = 16, else the strip
-  // kernel (measured: split-K wins where the tiled kernel cannot hold x,
-  // loses to it at 131072 x 3072 and to the strip kernel past M = 16); the
-  // GEMV again at M = 3, 4 where only the strip kernel would take the shape
+  // auto: the GEMV for M <= 2; from M = 3 the split-K MFMA kernel where it
+  // takes the shape (M <= 16; measured faster than the tiled kernel at every
+  // shape both take), else the tiled kernel, else the strip kernel; the GEMV
+  // again at M = 3, 4 where only the strip kernel would take the shape
   const bool splitk = mfma_splitk_supports(v, M), tiled = mfma_tiled_supports(v, M);
-  const bool split_first = splitk && M <= 16 && !tiled;
-  const bool auto_gemv = gemv_supports(v, M) && (M <= 2 || (!split_first && !tiled));
+  const bool auto_gemv = gemv_supports(v, M) && (M <= 2 || (!splitk && !tiled));
   if (kernel == SPECTRA_KERNEL_GEMV || (kernel == SPECTRA_KERNEL_AUTO && auto_gemv)) {
     if (!gemv_supports(v, M)) return fail(SPECTRA_E_UNSUPPORTED, "GEMV kernel cannot run this shape");
     return SPECTRA_PLAN_GEMV;
@@ -554,7 +552,7 @@ int plan_of(const DeviceView& v, int64_t M, int kernel) {
     case SPECTRA_KERNEL_MFMA_STRIP:
       return SPECTRA_PLAN_MFMA;
     default:
-      return tiled ? SPECTRA_PLAN_MFMA_TILED : (split_first ? SPECTRA_PLAN_MFMA_SPLITK : SPECTRA_PLAN_MFMA);
+      return splitk ? SPECTRA_PLAN_MFMA_SPLITK : (tiled ? SPECTRA_PLAN_MFMA_TILED : SPECTRA_PLAN_MFMA);
   }
 }
 

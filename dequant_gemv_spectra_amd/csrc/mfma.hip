@@ -671,38 +671,38 @@ __global__ __launch_bounds__(kKsThreads) void k_mfma_ks(const DeviceView v, cons
 }
 
 // ---------------------------------------------------------------------------
-// k_mfma_sk: the batched product for 1 <= M <= 32 with K split into ranges
-// of KR = 8 WG groups.  The other kernels stream a few records of many rows
-// per load instruction (16 rows x 64 bytes, or 8 rows x 128 bytes), and this
-// chip's memory system serves those at 4.0 - 4.9 TB/s where one row's 1 KB
-// per instruction streams at 6 TB/s.  Here block b takes K-range s = b % S
-// and walks 16-row tiles t = b / S, b / S + B / S, ...; consecutive blocks
-// read the ranges of one tile, so the chip still streams one moving window
-// of the code section.  Each wave moves two rows of a tile per step into an
-// LDS ring by LDS-DMA, one instruction per row (KR records, <= 1 KB), plus
-// the two rows' scales and zero bytes; the ring holds R tiles, R - 2 of them
-// in flight.  Wave w keeps x of its WG groups (all 16 MT rows) as MFMA A
-// operands in registers for the whole launch, so x is read from memory once
-// per block and never passes through LDS.  Per group: lane (r, c) reads word
-// r of row c's record from the tile, dequantizes it to exact fp16 (q - z),
-// one MFMA per m-subtile into a zero accumulator, and adds it with the
-// group's fp32 scale (the exact form of k_mfma_ks).  The waves' 16 x 16 MT
-// partials of a tile are summed through LDS in fixed order and stored as
-// fp32 to the workspace, P[s][m][n]; k_sk_sum adds the S ranges in order and
-// the heavy-tailed columns.
+// k_mfma_sk: the batched product for 1 <= M <= 16 with K split into S ranges
+// of KR = 16 WG <= 128 groups.  The other kernels stream a few records of
+// many rows per load instruction (16 rows x 64 bytes, or 8 rows x 128
+// bytes), and this chip's memory system serves those at 4.0 - 4.9 TB/s where
+// one row's 1 KB per instruction streams at 6 TB/s.  Here block b takes
+// K-range s = b % S and walks 16-row tiles t = b / S, b / S + B / S, ...;
+// consecutive blocks read the ranges of one tile, so the chip still streams
+// one moving window of the code section.  Each of the 16 waves moves one row
+// of a tile per step into an LDS ring by LDS-DMA: its records of the range in
+// two 1 KB instructions, its scales and its zero bytes in one 16-byte-per-lane
+// instruction each; the ring holds 3 tiles, 2 of them in flight while one is
+// computed.  Wave w keeps x of its WG groups (all 16 rows) as MFMA A operands
+// in registers for the whole launch, so x is read from memory once per block
+// and never passes through LDS.  Per group: lane (r, c) reads word r of row
+// c's record from the tile, dequantizes it to exact fp16 (q - z), one MFMA
+// into a zero accumulator, and adds it with the group's fp32 scale (the exact
+// form of k_mfma_ks).  The waves' 16 x 16 partials of a tile are summed
+// through LDS in fixed order and stored as fp32 to the workspace, P[s][m][n];
+// k_sk_sum adds the S ranges in order and the heavy-tailed columns.
 constexpr int kSkWaves = 16;  // 4 per SIMD: the LDS -> MFMA -> FMA chains of one hide behind the others
 constexpr int kSkThreads = 64 * kSkWaves;
-constexpr int kSkRow = 1040;   // LDS bytes per code row of a tile: 1 KB of DMA + 16 of pad (rows 4 banks apart)
+constexpr int kSkRow = 2064;   // LDS bytes per code row of a tile: 2 x 1 KB of DMA + 16 of pad (rows 4 banks apart)
 constexpr int kSkCodes = 16 * kSkRow;
-constexpr int kSkSRow = 136;   // per scale row: the 33 dwords holding its KR scales + 1 of pad (34 banks apart)
+constexpr int kSkSRow = 272;   // per scale row: 17 x 16 bytes holding its KR scales from the dword of its first (68 banks apart)
 constexpr int kSkScales = 16 * kSkSRow;
-constexpr int kSkZWave = 48;   // per wave: its row's 10 dwords of zero bytes + 2 of pad (rows 12 banks apart)
+constexpr int kSkZWave = 80;   // per wave: 5 x 16 bytes holding its row's zero bytes (rows 20 banks apart)
 constexpr int kSkZeros = kSkWaves * kSkZWave;
 constexpr int kSkSlot = kSkCodes + kSkScales + kSkZeros;
-constexpr int kSkDma = 3;      // DMA instructions per wave and tile
+constexpr int kSkDma = 4;      // DMA instructions per wave and tile
 template <int MT>
 constexpr int sk_ring() {
-  return MT == 1 ? 6 : 4;
+  return 3;
 }
 template <int MT>
 constexpr size_t sk_lds_bytes() {
@@ -753,7 +753,7 @@ __global__ __launch_bounds__(kSkThreads) void k_mfma_sk(const DeviceView v, cons
   constexpr int KR = kSkWaves * WG;
   constexpr int R = sk_ring<MT>();
   constexpr int D = R - 1;  // tiles in flight while one is computed
-  static_assert(WG >= 1 && WG <= 4, "groups per wave");
+  static_assert(WG >= 1 && WG <= 8 && MT == 1, "groups per wave, m-subtiles");
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -769,8 +769,10 @@ __global__ __launch_bounds__(kSkThreads) void k_mfma_sk(const DeviceView v, cons
   float4_t* part = reinterpret_cast<float4_t*>(smem + R * kSkSlot);  // [2][waves][MT][64]
   const uint64_t NG = (uint64_t)N * (uint64_t)G;
   const __amdgpu_buffer_rsrc_t rc = rsrc(v.codes, NG * 16);
-  const __amdgpu_buffer_rsrc_t rs = rsrc(v.scales, round4(NG * 2));
-  const __amdgpu_buffer_rsrc_t rz = rsrc(v.zeros, round4((NG + 1) / 2));
+  // 16-byte DMAs: a load straddling a descriptor's end would read as zeros
+  // in full, so the ranges are rounded up (sections are 256-byte padded)
+  const __amdgpu_buffer_rsrc_t rs = rsrc(v.scales, (NG * 2 + 15) & ~15ull);
+  const __amdgpu_buffer_rsrc_t rz = rsrc(v.zeros, ((NG + 1) / 2 + 15) & ~15ull);
 
   // Tile t into ring slot `slot`: this wave's rows 2w and 2w + 1 (the row
   // index is wave-uniform, so the offsets are a scalar base plus the lane).
@@ -782,10 +784,18 @@ __global__ __launch_bounds__(kSkThreads) void k_mfma_sk(const DeviceView v, cons
     const int64_t r0 = t * 16 + w;
     const bool ok0 = t < ntiles && r0 < N;
     const uint32_t f0 = (uint32_t)(r0 * G + g0);
-    const bool lc = lane < KR && g0 + lane < G;
-    dma16_nt(rc, base + (uint32_t)(w * kSkRow), ok0 && lc ? (f0 + lane) * 16u : kOob);
-    if (lane <= KR / 2) dma4(rs, base + (uint32_t)(kSkCodes + w * kSkSRow), ok0 ? ((f0 >> 1) + lane) * 4u : kOob);
-    if (lane < 10) dma4(rz, base + (uint32_t)(kSkCodes + kSkScales + w * kSkZWave), ok0 ? (((f0 >> 1) & ~3u) + 4u * lane) : kOob);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // the row's records of the range, 1 KB per instruction
+      const int gl = 64 * h + lane;
+      const bool lc = gl < KR && g0 + gl < G;
+      dma16_nt(rc, base + (uint32_t)(w * kSkRow + 1024 * h), ok0 && lc ? (f0 + gl) * 16u : kOob);
+    }
+    // scales from the dword holding the row's first (a row starts mid-dword
+    // when its flat index is odd), and the zero nibbles from the dword
+    // holding its first
+    if (lane < 17) dma16(rs, base + (uint32_t)(kSkCodes + w * kSkSRow), ok0 ? ((f0 >> 1) + 4 * lane) * 4u : kOob);
+    if (lane < 5)
+      dma16(rz, base + (uint32_t)(kSkCodes + kSkScales + w * kSkZWave), ok0 ? (((f0 >> 1) & ~3u) + 16u * lane) : kOob);
   };
 
   const int64_t t0 = blockIdx.x / S;
@@ -891,7 +901,7 @@ __global__ __launch_bounds__(kSkThreads) void k_mfma_sk(const DeviceView v, cons
 constexpr int kSumRows = 64;
 constexpr int kSumThreads = 256;
 constexpr int kSkMaxOut = 256;  // heavy-tailed columns k_sk_sum stages (LDS)
-constexpr int kSkMaxM = 32;
+constexpr int kSkMaxM = 16;
 constexpr int kSumLoads = (kSumRows * kSkMaxOut * 2 + 16 + 16 * kSumThreads - 1) / (16 * kSumThreads);
 constexpr int kSumXLoads = kSkMaxM * (kSkMaxOut / 8) / kSumThreads;
 
@@ -1001,7 +1011,7 @@ struct SkShape {
   int S, WG;  // K-ranges, groups per wave (a range is 8 WG groups)
 };
 SkShape sk_shape(const DeviceView& v) {
-  const int S = (v.G + 63) / 64;
+  const int S = (v.G + 127) / 128;
   const int per = (v.G + S - 1) / S;
   return SkShape{S, (per + 15) / 16};
 }
@@ -1020,7 +1030,7 @@ size_t sk_x_bytes(const DeviceView& v, int64_t M) {
 
 }  // namespace
 
-// The split-K kernel: 1 <= M <= 32, at most 256 heavy-tailed columns
+// The split-K kernel: 1 <= M <= 16, at most 256 heavy-tailed columns
 // (k_sk_sum stages them in LDS), code and outlier section offsets within 31
 // bits.
 bool mfma_splitk_supports(const DeviceView& v, int64_t M) {
@@ -1030,7 +1040,7 @@ bool mfma_splitk_supports(const DeviceView& v, int64_t M) {
   if ((uint64_t)v.N * (uint64_t)v.n_out * 2 >= 0x7FFFFFF0ull) return false;
   const int64_t KW = 32 * (int64_t)v.G + ((v.n_out + 31) & ~31);
   if (M * KW * 2 >= 0x7FFFFFFF) return false;
-  return M <= 16 ? sk_fits<1>(v) : sk_fits<2>(v);
+  return sk_fits<1>(v);
 }
 
 size_t mfma_splitk_workspace_bytes(const DeviceView& v, int64_t M) {
@@ -1176,6 +1186,10 @@ hipError_t launch_sk_mt(const DeviceView& v, const uint16_t* xw, int KW, int64_t
     case 2: return launch_sk_wg<MT, 2>(v, xw, KW, M, P, s, sh.S);
     case 3: return launch_sk_wg<MT, 3>(v, xw, KW, M, P, s, sh.S);
     case 4: return launch_sk_wg<MT, 4>(v, xw, KW, M, P, s, sh.S);
+    case 5: return launch_sk_wg<MT, 5>(v, xw, KW, M, P, s, sh.S);
+    case 6: return launch_sk_wg<MT, 6>(v, xw, KW, M, P, s, sh.S);
+    case 7: return launch_sk_wg<MT, 7>(v, xw, KW, M, P, s, sh.S);
+    case 8: return launch_sk_wg<MT, 8>(v, xw, KW, M, P, s, sh.S);
     default: return hipErrorNotSupported;
   }
 }
@@ -1183,7 +1197,7 @@ hipError_t launch_sk_mt(const DeviceView& v, const uint16_t* xw, int KW, int64_t
 hipError_t launch_sk(const DeviceView& v, const uint16_t* xw, int KW, int64_t M, uint16_t* y, void* workspace,
                      hipStream_t s) {
   float* P = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + sk_x_bytes(v, M));
-  const hipError_t e = M <= 16 ? launch_sk_mt<1>(v, xw, KW, M, P, s) : launch_sk_mt<2>(v, xw, KW, M, P, s);
+  const hipError_t e = launch_sk_mt<1>(v, xw, KW, M, P, s);
   if (e != hipSuccess) return e;
   const unsigned blocks = (unsigned)((v.N + kSumRows - 1) / kSumRows);
   const int S = sk_shape(v).S;
@@ -1191,10 +1205,8 @@ hipError_t launch_sk(const DeviceView& v, const uint16_t* xw, int KW, int64_t M,
     hipLaunchKernelGGL(k_sk_sum<1>, dim3(blocks), dim3(kSumThreads), 0, s, v, xw, KW, (int)M, S, P, y);
   else if (M <= 8)
     hipLaunchKernelGGL(k_sk_sum<2>, dim3(blocks), dim3(kSumThreads), 0, s, v, xw, KW, (int)M, S, P, y);
-  else if (M <= 16)
-    hipLaunchKernelGGL(k_sk_sum<4>, dim3(blocks), dim3(kSumThreads), 0, s, v, xw, KW, (int)M, S, P, y);
   else
-    hipLaunchKernelGGL(k_sk_sum<8>, dim3(blocks), dim3(kSumThreads), 0, s, v, xw, KW, (int)M, S, P, y);
+    hipLaunchKernelGGL(k_sk_sum<4>, dim3(blocks), dim3(kSumThreads), 0, s, v, xw, KW, (int)M, S, P, y);
   return hipGetLastError();
 }
 

@@ -128,15 +128,15 @@ typedef enum {
                                      SPECTRA_KERNEL_MFMA */
   SPECTRA_KERNEL_GEMV = 1,        /* VALU dequant-GEMV, x in LDS, fp32 accumulate; M <= 4, and
                                      K % 8 == 0 when M > 1 (else SPECTRA_E_UNSUPPORTED) */
-  SPECTRA_KERNEL_MFMA = 2,        /* the tiled kernel below where it takes the shape, else the
-                                     split-K kernel for M <= 16 where it does, else the strip kernel */
+  SPECTRA_KERNEL_MFMA = 2,        /* the split-K kernel below where it takes the shape, else the
+                                     tiled kernel where it does, else the strip kernel */
   SPECTRA_KERNEL_MFMA_TILED = 3,  /* 16-row tiles with K split over 8 waves: M <= 16, the M rows of
                                      x in LDS */
   SPECTRA_KERNEL_MFMA_STRIP = 4,  /* one 16-row strip per wave for the whole K loop: any shape the
                                      MFMA path takes */
   SPECTRA_KERNEL_MFMA_SPLITK = 5  /* K split in ranges over blocks, x of a range held in registers,
-                                     fp32 partial sums in the workspace: M <= 32, an even number of
-                                     32-member groups per row, at most 256 heavy-tailed columns */
+                                     fp32 partial sums in the workspace: M <= 16, at most 256
+                                     heavy-tailed columns */
 } spectra_kernel;
 
 typedef struct {

@@ -379,13 +379,11 @@ def test_grouped_launch_chunks_and_mixed_lengths():
 
 def test_kernel_plan_follows_the_selection_rule():
     """spectra_gemm_plan names what spectra_gemm_ex runs: the GEMV up to M = 2,
-    from M = 3 the tiled MFMA kernel where it runs the shape, the split-K
-    kernel up to M = 16 where the tiled one does not (here: more groups per
-    row than the tiled kernel holds), the strip kernel past both; the GEMV
-    again at M = 3, 4 where only the strip kernel would take the shape (here:
-    more heavy-tailed columns than the split-K and tiled kernels stage).  Each
-    MFMA kernel can be forced, and a forced kernel that cannot run the shape
-    is refused."""
+    from M = 3 the split-K MFMA kernel where it runs the shape (M <= 16), the
+    strip kernel past it; the GEMV again at M = 3, 4 where only the strip
+    kernel would take the shape (here: more heavy-tailed columns than the
+    split-K and tiled kernels stage).  Each MFMA kernel can be forced, and a
+    forced kernel that cannot run the shape is refused."""
     sp = _sp()
     from dequant_gemv_spectra_amd import synth as S
     W, g, _ = S.random_case(100, 4096, 40, 90)
@@ -396,20 +394,19 @@ def test_kernel_plan_follows_the_selection_rule():
     W, g, _ = S.random_case(40, 15000, 100, 92)
     c15k, _ = check_pack(W, g)
     assert [sp.spectra_gemm_plan(c4k, M) for M in (1, 2, 3, 4, 8, 16, 17, 32, 33)] == \
-        ["k_gemv_m1"] * 2 + ["k_mfma_ks"] * 4 + ["k_mfma"] * 3
-    assert sp.spectra_gemm_plan(c4k, 32, kernel="mfma_splitk") == "k_mfma_sk"
-    assert sp.spectra_gemm_plan(c4k, 8, kernel="mfma_splitk") == "k_mfma_sk"
+        ["k_gemv_m1"] * 2 + ["k_mfma_sk"] * 4 + ["k_mfma"] * 3
+    assert sp.spectra_gemm_plan(c4k, 8, kernel="mfma_tiled") == "k_mfma_ks"
     assert [sp.spectra_gemm_plan(cout, M) for M in (1, 2, 3, 4, 5)] == ["k_gemv_m1"] * 4 + ["k_mfma"]
     assert [sp.spectra_gemm_plan(c15k, M) for M in (1, 2, 3, 5, 33)] == ["k_gemv_m1"] * 2 + ["k_mfma_sk"] * 2 + ["k_mfma"]
     assert sp.spectra_gemm_plan(c4k, 3, kernel="gemv") == "k_gemv_m1"
-    assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma") == "k_mfma_ks"
+    assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma") == "k_mfma_sk"
     assert sp.spectra_gemm_plan(c15k, 1, kernel="mfma") == "k_mfma_sk"
     assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma_tiled") == "k_mfma_ks"
     assert sp.spectra_gemm_plan(c4k, 1, kernel="mfma_strip") == "k_mfma"
     assert sp.spectra_gemm_plan(cout, 5, kernel="mfma") == "k_mfma"
     for h, M, kernel in ((c4k, 8, "gemv"),          # the GEMV takes M <= 4
                          (c4k, 17, "mfma_tiled"),   # the tiled kernel M <= 16
-                         (c4k, 33, "mfma_splitk"),  # the split-K kernel M <= 32
+                         (c4k, 17, "mfma_splitk"),  # the split-K kernel M <= 16
                          (cout, 3, "mfma_splitk")):  # and at most 256 heavy-tailed columns
         with pytest.raises(sp.SpectraError) as ei:
             sp.spectra_gemm_plan(h, M, kernel=kernel)
@@ -548,19 +545,19 @@ def test_mfma_product_small(N, K, n_out, seed, M):
 
 
 SPLITK_CASES = [  # (N, K, planted heavy-tailed channels, seed, M): groups per row G, K-ranges S, groups per wave WG
-    (100, 1000, 8, 201, 5),     # G 32, S 1, WG 4
-    (77, 2048, 0, 202, 16),     # G 64, S 1, WG 8
-    (130, 2600, 30, 203, 17),   # G 81 (odd: rows start mid-dword), S 2, WG 6, two m-subtiles
+    (100, 1000, 8, 201, 5),     # G 32, S 1, WG 2
+    (77, 2048, 0, 202, 16),     # G 64, S 1, WG 4
+    (130, 2600, 30, 203, 15),   # G 81 (odd: rows start mid-dword), S 1, WG 6
     (45, 520, 5, 204, 1),       # G 17, M = 1
-    (300, 4100, 90, 205, 32),   # G 126, S 2, 78 heavy-tailed columns
-    (64, 8192, 82, 206, 12),    # G 255, S 4
-    (257, 3072, 31, 207, 2),    # G 96, S 2, WG 6
-    (33, 1500, 300, 208, 9),    # 97 heavy-tailed columns, G 44
-    (200, 9728, 150, 209, 7),   # G 301, S 5, last range 45 groups
-    (513, 6000, 60, 210, 24),   # G 186, S 3
-    (40, 12000, 250, 211, 3),   # G 372, S 6
-    (128, 300, 6, 215, 31),     # G 10, WG 2: waves 5 .. 7 have no group
-    (17, 2100, 20, 213, 4),     # G 66, one ragged tile
+    (300, 4100, 90, 205, 16),   # G 126, S 1, WG 8, 78 heavy-tailed columns
+    (64, 8192, 82, 206, 12),    # G 255, S 2
+    (257, 3072, 31, 207, 2),    # G 96, WG 6
+    (33, 1500, 300, 208, 9),    # 97 heavy-tailed columns, G 44, WG 3
+    (200, 9728, 150, 209, 7),   # G 301, S 3, WG 7, last range 99 groups
+    (513, 6000, 60, 210, 13),   # G 186, S 2
+    (40, 12000, 250, 211, 3),   # G 372, S 3
+    (128, 300, 6, 215, 14),     # G 10, WG 1: waves 10 .. 15 have no group
+    (17, 2100, 20, 213, 4),     # G 66, WG 5, one ragged tile
 ]
 
 
@@ -578,9 +575,9 @@ def test_splitk_product(N, K, n_out, seed, M):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("N,K,n_out,seed,M", [(60000, 256, 3, 222, 8), (29000, 2048, 20, 223, 20)])
+@pytest.mark.parametrize("N,K,n_out,seed,M", [(60000, 256, 3, 222, 8), (29000, 2048, 20, 223, 10)])
 def test_splitk_many_tiles_per_block(N, K, n_out, seed, M):
-    """Enough 16-row tiles that every block's LDS ring wraps several times
+    """Enough 16-row tiles that every block's LDS ring wraps many times
     (15 and 7 tiles per block on 256 compute units): every element of the
     first, sampled rows of the rest."""
     sp = _sp()

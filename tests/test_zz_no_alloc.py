@@ -50,10 +50,10 @@ def test_noalloc_refuses_a_workspace_past_its_scratch():
 def test_noalloc_runs_split_k_and_falls_back_past_its_scratch():
     """The split-K kernel under the no-allocation entry point: bit-equal to
     spectra_gemm_ex while its fp32 partial sums fit the 8 MiB scratch; past
-    that (here 6 K-ranges x 16 rows x 24000 outputs x 4 bytes, on a shape the
-    tiled kernel declines, so that the default runs split-K) the entry point
-    runs the strip kernel instead, within the oracle bound on sampled rows,
-    and refuses split-K when it is forced."""
+    that (here 3 K-ranges x 16 rows x 48000 outputs x 4 bytes, on a shape the
+    tiled kernel declines) the entry point runs the strip kernel instead,
+    within the oracle bound on sampled rows, and refuses split-K when it is
+    forced."""
     import torch
     from dequant_gemv_spectra_amd import spectra as sp
     W, g, _ = synth.random_case(3000, 2048, 20, 125)
@@ -71,17 +71,17 @@ def test_noalloc_runs_split_k_and_falls_back_past_its_scratch():
         err = np.abs(y.cpu().numpy().astype(np.float64) - O.matmul_ref(W_hat, x))
         assert (err <= O.tolerance(W_hat, x)).all()
     c.close()
-    W, g, _ = synth.random_case(24000, 12000, 100, 126)
+    W, g, _ = synth.random_case(48000, 12000, 100, 126)
     c = sp.spectra_pack(W, g)
     del W
     img = sp.spectra_export(c)
     M = 16
     assert sp.spectra_gemm_plan(c, M) == "k_mfma_sk"
     x = rng.standard_normal((M, 12000)).astype(np.float16)
-    y = torch.full((M, 24000), 3.0, dtype=torch.float16, device="cuda")
+    y = torch.full((M, 48000), 3.0, dtype=torch.float16, device="cuda")
     sp.spectra_gemm_noalloc(c, torch.from_numpy(x).cuda(), y)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.arange(512), rng.integers(0, 24000, 1500), np.arange(23700, 24000)]))
+    rows = np.unique(np.concatenate([np.arange(512), rng.integers(0, 48000, 1500), np.arange(47700, 48000)]))
     W_hat = O.reconstruct_rows(img, rows)
     err = np.abs(y.cpu().numpy()[:, rows].astype(np.float64) - O.matmul_ref(W_hat, x))
     assert (err <= O.tolerance(W_hat, x)).all()
