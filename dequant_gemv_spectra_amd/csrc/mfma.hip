@@ -978,25 +978,42 @@ __global__ __launch_bounds__(kSumThreads) void k_sk_sum(const DeviceView v, cons
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) acc[i] += pv[i][kk];
   }
+  // heavy-tailed columns two at a time on v_dot2: the row's weights start at
+  // any half (two 16-bit reads make a pair), x rows at 16-byte boundaries
+  // (one 32-bit read); a last odd column pairs with a zero weight
   const uint16_t* orow = reinterpret_cast<const uint16_t*>(ob) + oh + nl * n_out;
+  const int np = n_out >> 1;
   int j = 0;
-  for (; j + 4 <= n_out; j += 4) {
-    float o[4], xv[MI][4];
+  for (; j + 4 <= np; j += 4) {
+    uint32_t o2[4], x2[MI][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = h2f(orow[j + u]);
+    for (int e = 0; e < 4; ++e) o2[e] = (uint32_t)orow[2 * (j + e)] | ((uint32_t)orow[2 * (j + e) + 1] << 16);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) xv[i][u] = h2f(xo[mrow[i] * XS + j + u]);
+      for (int e = 0; e < 4; ++e) x2[i][e] = reinterpret_cast<const uint32_t*>(xo + mrow[i] * XS)[j + e];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int i = 0; i < MI; ++i) acc[i] += xv[i][u] * o[u];
+      for (int i = 0; i < MI; ++i)
+        acc[i] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, o2[e]), __builtin_bit_cast(half2_t, x2[i][e]),
+                                        acc[i], false);
   }
-  for (; j < n_out; ++j) {
-    const float o = h2f(orow[j]);
+  for (; j < np; ++j) {
+    const uint32_t o2 = (uint32_t)orow[2 * j] | ((uint32_t)orow[2 * j + 1] << 16);
 #pragma unroll
-    for (int i = 0; i < MI; ++i) acc[i] += h2f(xo[mrow[i] * XS + j]) * o;
+    for (int i = 0; i < MI; ++i)
+      acc[i] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, o2),
+                                      __builtin_bit_cast(half2_t, reinterpret_cast<const uint32_t*>(xo + mrow[i] * XS)[j]),
+                                      acc[i], false);
+  }
+  if (n_out & 1) {
+    const uint32_t o2 = (uint32_t)orow[n_out - 1];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      acc[i] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, o2),
+                                      __builtin_bit_cast(half2_t, reinterpret_cast<const uint32_t*>(xo + mrow[i] * XS)[np]),
+                                      acc[i], false);
   }
 #pragma unroll
   for (int i = 0; i < MI; ++i)
