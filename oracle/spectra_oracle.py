@@ -43,8 +43,8 @@ Parity status of each function (what pins it, in tests/test_oracle_pins.py):
   pack / unpack      hand-written byte fixtures in tests/golden, round trip,
                      footprint closed form, outlier bits
   matmul_ref         pure-Python brute force on tiny shapes, one-hot inputs
-  tolerance          definition written in the header; no independent pin
-                     beyond its use (parity unpinned as a formula)
+  tolerance          hand-computed bounds on a 3 x 2 W_hat and two rows of x
+                     (signs on both operands), and the 1e-6 floor
   embed_ref          grid-valued tables gather back bit-exact (bulk and
                      heavy-tailed channels), out-of-range ids give zero rows
   kv_quantize        grid-valued head vectors round-trip exactly; the same

@@ -333,11 +333,16 @@ def test_one_hot_inputs_select_columns():
 
 
 def test_tolerance_definition_shape_and_floor():
-    W_hat = np.array([[1.0, -2.0], [0.0, 0.0]])
-    x = np.array([[3.0, 1.0]], np.float16)
+    # by hand: |W_hat| |x|^T for W_hat rows (1, -2), (0, 0), (-4, 0.5) and
+    # x rows (3, 1), (-2, -6): row 0 of x gives 5, 0, 12.5; row 1 gives 14,
+    # 0, 11 (an absolute value dropped on either operand, or W_hat not
+    # transposed, changes every one of them)
+    W_hat = np.array([[1.0, -2.0], [0.0, 0.0], [-4.0, 0.5]])
+    x = np.array([[3.0, 1.0], [-2.0, -6.0]], np.float16)
     t = O.tolerance(W_hat, x)
-    assert t.shape == (1, 2)
-    assert t[0, 0] == pytest.approx(1e-3 * 5 + 1e-6) and t[0, 1] == pytest.approx(1e-6)
+    assert t.shape == (2, 3)
+    np.testing.assert_allclose(t, 1e-3 * np.array([[5.0, 0.0, 12.5], [14.0, 0.0, 11.0]]) + 1e-6, rtol=1e-12)
+    assert t[0, 1] == t[1, 1] == pytest.approx(1e-6)  # the floor
 
 
 # --------------------------------------------------------------------------
