@@ -760,7 +760,14 @@ __global__ __launch_bounds__(kSkThreads) void k_mfma_sk(const DeviceView v, cons
   const int r4 = lane >> 4, c = lane & 15;
   const int G = v.G;
   const int64_t N = v.N;
-  const int s = (int)(blockIdx.x % (unsigned)S);
+  // Blocks are dispatched to the 8 XCDs in turn (block b on XCD b % 8).  When
+  // the grid is a multiple of 8 S, the S ranges of a tile go to blocks 8
+  // apart, i.e. to one XCD, whose L2 then serves the cache lines two ranges
+  // (and two rows) share; else to consecutive blocks.
+  const unsigned bid = blockIdx.x;
+  const bool xcd = gridDim.x % (8u * (unsigned)S) == 0;
+  const unsigned lane8 = bid & 7u, j8 = bid >> 3;
+  const int s = (int)(xcd ? j8 % (unsigned)S : bid % (unsigned)S);
   const int64_t Bs = gridDim.x / S;
   const int64_t ntiles = (N + 15) / 16;
   const int g0 = KR * s;
@@ -798,7 +805,7 @@ __global__ __launch_bounds__(kSkThreads) void k_mfma_sk(const DeviceView v, cons
       dma16(rz, base + (uint32_t)(kSkCodes + kSkScales + w * kSkZWave), ok0 ? (((f0 >> 1) & ~3u) + 16u * lane) : kOob);
   };
 
-  const int64_t t0 = blockIdx.x / S;
+  const int64_t t0 = xcd ? (int64_t)(j8 / (unsigned)S) * 8 + lane8 : (int64_t)(bid / (unsigned)S);
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(t0 + d * Bs, d);
 
