@@ -675,10 +675,10 @@ __global__ __launch_bounds__(kKsThreads) void k_mfma_ks(const DeviceView v, cons
 // of KR = 16 WG <= 128 groups.  The other kernels stream a few records of
 // many rows per load instruction (16 rows x 64 bytes, or 8 rows x 128
 // bytes), and this chip's memory system serves those at 4.0 - 4.9 TB/s where
-// one row's 1 KB per instruction streams at 6 TB/s.  Here block b takes
-// K-range s = b % S and walks 16-row tiles t = b / S, b / S + B / S, ...;
-// consecutive blocks read the ranges of one tile, so the chip still streams
-// one moving window of the code section.  Each of the 16 waves moves one row
+// one row's 1 KB per instruction streams at 6 TB/s.  Here each block takes
+// one K-range and walks 16-row tiles t0, t0 + B / S, ...; the S blocks on
+// the ranges of one tile are 8 apart (one XCD, see below), so the chip still
+// streams one moving window of the code section.  Each of the 16 waves moves one row
 // of a tile per step into an LDS ring by LDS-DMA: its records of the range in
 // two 1 KB instructions, its scales and its zero bytes in one 16-byte-per-lane
 // instruction each; the ring holds 3 tiles, 2 of them in flight while one is
@@ -1032,7 +1032,7 @@ __global__ __launch_bounds__(kSumThreads) void k_sk_sum(const DeviceView v, cons
 namespace {
 
 struct SkShape {
-  int S, WG;  // K-ranges, groups per wave (a range is 8 WG groups)
+  int S, WG;  // K-ranges, groups per wave (a range is 16 WG groups, one per wave of 16)
 };
 SkShape sk_shape(const DeviceView& v) {
   const int S = (v.G + 127) / 128;
