@@ -323,6 +323,36 @@ def test_config3_layers_as_the_benchmark_launches_them():
 
 
 @pytest.mark.timeout(900)
+def test_config3_every_layer_image_matches_oracle_hash():
+    """Every one of the 252 linears of the 36-layer 4B-class stack packed on
+    the GPU: its container image hashes to the oracle's image, whose SHA-256
+    tests/golden/make_cfg3_image_hashes.py wrote by calling only the CPU
+    oracle (which also recorded that no channel lies within rounding of the
+    kurtosis threshold, so one mask is the only valid one)."""
+    import hashlib
+    sp = _sp()
+    ref = {}
+    with open(os.path.join(GOLDEN, "cfg3_image_sha256.txt")) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, N, K, n_out, border, size, sha = line.split()
+            ref[name] = (int(N), int(K), int(n_out), int(border), int(size), sha)
+    wl = synth.workload(3)
+    assert len(ref) == len(wl.linears) == 252
+    for lin in wl.linears:
+        N, K, n_out, border, size, sha = ref[lin.name]
+        assert (N, K, border) == (lin.N, lin.K, 0)
+        W, g = synth.weights(lin, 3), synth.gamma(lin, 3)
+        c = sp.spectra_pack(W, g)
+        del W
+        assert c.info()["n_out"] == n_out, lin.name
+        img = sp.spectra_export(c)
+        c.close()
+        assert len(img) == size and hashlib.sha256(img).hexdigest() == sha, f"{lin.name}: image differs from the oracle's"
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [4, 5])
 def test_config_large(cfg):
     wl = synth.workload(cfg)
