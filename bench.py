@@ -86,7 +86,7 @@ def log(msg):
 
 GEMV_SOURCES = ("gemv.hip", "gemv_common.h")
 MFMA_SOURCES = ("mfma.hip",)
-STEP_SOURCES = ("step.hip", "gemv_common.h")
+STEP_SOURCES = ("step.hip", "gemv_common.h", "gemv.hip")  # gemv.hip picks the step's team width too
 
 
 def kernel_sources_sha(files=GEMV_SOURCES):

@@ -497,7 +497,15 @@ struct Variant {
 
 // Lanes-per-row L and slots-per-lane P = ceil(G/L) with the best lane use
 // (ties: fewer slots, i.e. fewer registers).  P == 0: no variant fits.
-Variant pick_variant(int G) {
+// One exception, measured: with one row of x and 64 < G <= 96, 32-lane teams
+// (3 slots; 83 % of the lanes busy at G = 80) beat fully used 16-lane teams
+// (5 slots).  A short launch's block then walks twice as many tiles of half
+// the rows, so one tile's transfer overlaps the previous one's arithmetic
+// (the 4B-class decode step's q/k/v and gate/up launches at K = 2560: step
+// 1.046 -> 1.008 ms, gate/up 9.7 -> 8.9 us); a long launch at G = 80 was
+// unchanged, and at G = 48 (K = 1536) the 32-lane teams were slower.
+Variant pick_variant(int G, int mx) {
+  if (mx == 1 && G > 64 && G <= 96) return Variant{32, (G + 31) / 32};
   Variant best{64, 0};
   double best_eff = -1.0;
   const int Ls[3] = {64, 32, 16};
@@ -674,7 +682,7 @@ hipError_t launch_tasks(GemvTasks& ts, int64_t M, hipStream_t s) {
     const size_t b = lds_bytes(ts.t[i].v, mx);
     if (b > lds) lds = b;
   }
-  const Variant vr = pick_variant(gmax);
+  const Variant vr = pick_variant(gmax, mx);
   if (vr.P == 0 || lds > lds_limit(ts.t[0].v)) return hipErrorNotSupported;
   switch (mx) {
     case 1: return launch_mx<1>(vr.L, vr.P, ts, lds, s, (int32_t)M);
@@ -686,7 +694,7 @@ hipError_t launch_tasks(GemvTasks& ts, int64_t M, hipStream_t s) {
 }  // namespace
 
 bool gemv_variant(int G, int* L, int* P) {
-  const Variant vr = pick_variant(G);
+  const Variant vr = pick_variant(G, 1);
   *L = vr.L;
   *P = vr.P;
   return vr.P > 0;
@@ -698,7 +706,7 @@ bool gemv_supports(const DeviceView& v, int64_t M) {
   if (M > 1 && v.K % 8 != 0) return false;  // each row of x must start 16-byte aligned
   // a block stages at most kXChunks * 8 * kBlock channels and kQuads * 4 * kBlock bulk positions
   if (v.K > kXChunks * 8 * kBlock || (int64_t)kGroup * v.G > (int64_t)kQuads * 4 * kBlock) return false;
-  const int P = pick_variant(v.G).P;
+  const int P = pick_variant(v.G, batch_tile(M)).P;
   if (P == 0 || P > max_slots(batch_tile(M))) return false;
   return lds_bytes(v, batch_tile(M)) <= lds_limit(v);
 }
