@@ -282,8 +282,8 @@ def test_config_full(cfg):
 def test_config3_layers_as_the_benchmark_launches_them():
     """Layers 0, 17 and 35 of the 4B-class stack: every container image equal
     to the oracle's, then the benchmark's four launches per layer -- grouped
-    q/k/v (one tile per block), o, grouped gate/up (three tiles per block on
-    the register-held-x path) and down -- checked against the oracle on
+    q/k/v (two tiles per block, 32-lane teams), o, grouped gate/up (five
+    tiles per block on the register-held-x path) and down -- checked against the oracle on
     sampled rows, and the grouped outputs bit-equal to single launches of
     containers with the same group count."""
     sp, torch = _sp(), _torch()
